@@ -1,0 +1,61 @@
+"""Pins of the oracle's assembly of one prefill call (packing, reuse import, head map)."""
+import math
+
+import numpy as np
+import torch
+
+import workloads
+from oracle import reference
+
+
+def complex_rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """RoPE of x [..., n, D] at positions pos [n], as a complex multiplication of rotate-half pairs."""
+    D = x.shape[-1]
+    th = base ** (-np.arange(D // 2) * 2.0 / D)
+    z = (x[..., : D // 2] + 1j * x[..., D // 2:]) * np.exp(1j * pos[:, None] * th)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def test_packed_call_matches_per_head_loops():
+    """Unpacking [total_q][H][D] into per-head rows: checked with explicit loops over (seq, head, row)."""
+    wl = workloads.random_small(3, torch.float32, allow_reuse=False)
+    inp = workloads.make_inputs(wl)
+    o, lse = reference.prefill(inp)
+    cu = wl.cu_q()
+    G = wl.group
+    for b in range(wl.num_seqs):
+        L = wl.kv_lens[b]
+        for h in range(wl.num_q_heads):
+            g = h // G
+            cls = int(wl.head_class[0, g])
+            for t in range(0, L, max(1, L // 7)):
+                qv = inp.q[cu[b] + t, h].double().numpy()
+                ks = inp.k_new[cu[b]:cu[b] + L, g].double().numpy()
+                vs = inp.v_new[cu[b]:cu[b] + L, g].double().numpy()
+                vis = [j for j in range(L) if j <= t and (cls == 1 or j < wl.sink or j > t - wl.window)]
+                s = ks[vis] @ qv / math.sqrt(wl.head_dim)
+                mx = s.max()
+                p = np.exp(s - mx)
+                assert abs(lse[h, cu[b] + t] - (mx + math.log(p.sum()))) < 1e-10
+                np.testing.assert_allclose(o[cu[b] + t, h], p @ vs[vis] / p.sum(), rtol=0, atol=1e-10)
+
+
+def test_reused_keys_equal_direct_rope_at_actual_position():
+    """Offline keys = RoPE(raw, offline pos); after import they must equal RoPE(raw, actual pos)."""
+    wl = workloads.Workload(name="reuse pin", config_id=900, num_layers=1, layer=0, kv_lens=[96], q_starts=[64],
+                            num_q_heads=2, num_kv_heads=2, head_dim=16, page_size=16, sink=2, window=8,
+                            dtype=torch.float32, head_class=np.array([[1, 0]], np.uint8), doc_len=32,
+                            rope_base=1e4)
+    inp = workloads.make_inputs(wl)
+    raw = {}
+    for d in inp.docs:
+        r = np.random.Generator(np.random.PCG64(d.tok_begin)).standard_normal((2, d.n_tok, 16))
+        off_pos = d.offline_start + np.arange(d.n_tok)
+        d.k_off = torch.from_numpy(complex_rope(r, off_pos, wl.rope_base)).float()
+        raw[d.tok_begin] = r
+    k, v = reference.sequence_kv(inp, 0)
+    for d in inp.docs:
+        want = complex_rope(raw[d.tok_begin], d.tok_begin + np.arange(d.n_tok), wl.rope_base)
+        np.testing.assert_allclose(k[:, d.tok_begin:d.tok_begin + d.n_tok], want, rtol=0, atol=2e-5)
+        assert d.delta != 0
+    np.testing.assert_array_equal(k[:, 64:], inp.k_new.double().numpy().transpose(1, 0, 2))
