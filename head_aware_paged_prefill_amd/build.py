@@ -1,0 +1,53 @@
+"""Build librk_seg.so in-tree: host core with g++, gfx950 kernels with hipcc, linked by hipcc.
+
+    python -m head_aware_paged_prefill_amd.build [--checked]
+
+Every HIP line carries `-Xclang -target-feature -Xclang -packed-fp32-ops` (packed fp32 VALU ops off).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "librk_seg.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+              "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build step failed: " + " ".join(cmd[:3]) + " ...")
+    return r
+
+
+def build(verbose: bool = False, out: str = LIB, extra_hip: list | None = None) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    inc = ["-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
+    host_o = os.path.join(BUILD, "rk_host.o")
+    kern_o = os.path.join(BUILD, "rk_kernels.o")
+    _run(["g++"] + HOST_FLAGS + inc + ["-c", os.path.join(CSRC, "rk_host.cpp"), "-o", host_o], verbose)
+    _run([HIPCC] + HIP_FLAGS + (extra_hip or []) + inc + ["-c", os.path.join(CSRC, "rk_kernels.hip"), "-o", kern_o],
+         verbose)
+    tmp = out + ".tmp"
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", host_o, kern_o, "-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,232 @@
+/*
+ * rk_seg.h -- C ABI of the SegPagedAttention prefill library for AMD MI355X (gfx950).
+ *
+ * What the library computes.  The KV cache is kept in pages owned by one
+ * (layer, KV head, sequence).  Heads are classified once, offline, as GLOBAL or
+ * LOCAL; the class map is an input read by table lookup with no online cost
+ * (page "RedKnot - Xiaohongshuが開発した…" (aiboss88.com), section RedKnotの使い方,
+ * PROFILE item, and section 主な利点, second item).  GLOBAL heads hold and read
+ * every context page; LOCAL heads physically hold only the sink pages and the
+ * pages of a recent window (page "为什么长上下文推理这么慢？RedKnot如何用1个百分点的
+ * 质量代价换来2–5倍TTFT加速" (bjdmk.com.cn), section 二 ③ SegPagedAttention).
+ * Attention runs without any attention mask: visibility is derived from token
+ * indices inside the kernel (same page, section 二 ③; aiboss88.com, section 技術原則,
+ * fourth item).  Reused document keys are rotated from their offline to their
+ * actual position before use (page "RedKnot – 小红书研发并开源的长上下文大模型推理引擎"
+ * (shshi.cn), section RedKnot技术原理, 2. 位置无关缓存复用).
+ *
+ * Visibility (token indices; i = absolute query position, j = key position):
+ *   GLOBAL: j <= i.       LOCAL: j <= i and (j < sink or j > i - window).
+ * The window holds `window` keys including the query; the sink is the first
+ * `sink` absolute positions of the sequence.  Query head h reads KV head
+ * h / (num_q_heads / num_kv_heads); the class is per (layer, KV head).
+ *
+ * Memory layout (all device buffers are caller-owned; the library allocates no
+ * device memory):
+ *   K pages   [num_pages][page_size][head_dim]   (token-major)
+ *   V pages   [num_pages][head_dim][page_size]   (channel-major: each page stores V transposed)
+ *   q, o      [total_q][num_q_heads][head_dim]   queries packed by sequence, in sequence order
+ *   k_new, v_new [total_q][num_kv_heads][head_dim]  keys/values of the query tokens
+ *   lse       [num_q_heads][total_q] fp32, natural log
+ * where sequence b contributes kv_len[b] - q_start[b] query tokens at absolute
+ * positions q_start[b] .. kv_len[b]-1.  Element type: RK_BF16 (bfloat16) or RK_F32.
+ * Every device pointer must be 16-byte aligned; head_dim is 64 or 128; page_size
+ * is a power of two in [8, 256].
+ *
+ * Cache contents contract: before attention, every slot of a held page whose
+ * token is below kv_len must have been written -- by the append inside
+ * rk_seg_attn_prefill (tokens >= q_start) or by rk_seg_reuse_rerotate (tokens
+ * below q_start).  Slots at or beyond kv_len and pages a head does not hold may
+ * contain any bits (NaN included); they never reach the output.
+ *
+ * Errors: every call returns an rk_status; no exception crosses the ABI.  On
+ * failure, rk_last_error() returns a thread-local message.  A failed call
+ * leaves the pool and tables unchanged.
+ *
+ * Threads and streams: a pool and its tables are not thread-safe; callers
+ * serialise calls on one pool.  Device work is enqueued on the given HIP stream
+ * (void * holding a hipStream_t; NULL = the null stream) and is asynchronous;
+ * host-side state (free list, tables) changes synchronously.  Pages returned to
+ * the free list may be handed out again at once: device work that uses them must
+ * be ordered after earlier work on them (same stream, or caller synchronisation).
+ */
+#ifndef RK_SEG_H
+#define RK_SEG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t rk_status;
+#define RK_OK 0
+#define RK_ERR_INVALID_ARG (-1)
+#define RK_ERR_OUT_OF_PAGES (-2)
+#define RK_ERR_WORKSPACE_TOO_SMALL (-3)
+#define RK_ERR_UNSUPPORTED (-4)
+#define RK_ERR_HIP (-5)
+#define RK_ERR_STATE (-6)
+#define RK_ERR_INTERNAL (-7)
+
+#define RK_LOCAL 0
+#define RK_GLOBAL 1
+
+#define RK_BF16 0
+#define RK_F32 1
+
+#define RK_ROPE_ROTATE_HALF 0 /* pairs (m, m + D/2) */
+#define RK_ROPE_INTERLEAVED 1 /* pairs (2m, 2m + 1) */
+
+typedef struct rk_pool rk_pool;
+typedef struct rk_tables rk_tables;
+
+/* Pool description.  k_pages / v_pages: device, caller-owned, layout above, 16-byte aligned.
+ * initial_free_order: host, optional (NULL = ascending ids); a permutation of [0, num_pages)
+ * giving the free list from its head.  The array is copied. */
+typedef struct {
+  int32_t num_layers;
+  int32_t num_kv_heads;
+  int32_t head_dim;  /* 64 or 128 */
+  int32_t page_size; /* power of two, 8..256 */
+  int32_t dtype;     /* RK_BF16 or RK_F32 */
+  int32_t reserved0;
+  int64_t num_pages; /* >= 0, < 2^31 */
+  void *k_pages;
+  void *v_pages;
+  const int32_t *initial_free_order;
+} rk_pool_desc;
+
+/* One prefill call over layers [layer_begin, layer_end) of a batch of sequences.
+ * q_start, kv_len: host [num_seqs], 0 <= q_start[b] <= kv_len[b] < 2^31.
+ * head_class: host [num_layers * num_kv_heads], row-major by layer, values RK_LOCAL / RK_GLOBAL.
+ * sink >= 0, window >= 1.  num_q_heads must be a positive multiple of the pool's num_kv_heads.
+ * All host arrays are copied. */
+typedef struct {
+  int32_t layer_begin;
+  int32_t layer_end;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  const int32_t *q_start;
+  const int32_t *kv_len;
+  const uint8_t *head_class;
+  int32_t sink;
+  int32_t window;
+} rk_batch_desc;
+
+/* Counters of one built call (host, exact integers). */
+typedef struct {
+  int64_t pages_held;        /* pages the call holds over all its layers */
+  int64_t total_q;           /* query tokens per layer */
+  int64_t visible_pairs;     /* sum over layers, q heads and queries of |visible keys| */
+  int64_t visible_pairs_global; /* the part from GLOBAL heads */
+  int64_t work_items;        /* attention work items over all layers */
+  int64_t key_tiles;         /* key tiles the items visit over all layers */
+  int64_t workspace_bytes;   /* device workspace the build uses */
+} rk_tables_stats;
+
+/* -- pool ---------------------------------------------------------------------------------- */
+
+/* Create a pool over caller-owned page storage.  Host only: no device work.
+ * Storage assumption: page p of the K array starts at k_pages + p*page_size*head_dim elements,
+ * of the V array at v_pages + p*head_dim*page_size elements.  Errors: RK_ERR_INVALID_ARG. */
+rk_status rk_seg_pool_create(const rk_pool_desc *desc, rk_pool **out);
+
+/* Destroy a pool.  Fails with RK_ERR_STATE while tables built from it are alive. */
+rk_status rk_seg_pool_destroy(rk_pool *pool);
+
+/* Free and used page counts (free + used == num_pages). */
+rk_status rk_seg_pool_query(const rk_pool *pool, int64_t *free_pages, int64_t *used_pages);
+
+/* Copy up to cap ids of the free list, head first, into out; *n = its full length. */
+rk_status rk_seg_pool_free_list(const rk_pool *pool, int32_t *out, int64_t cap, int64_t *n);
+
+/* -- tables: SELECTVISIBLESTATE (page "RedKnot - Xiaohongshuが開発した…", section 使い方) ---------- */
+
+/* Device workspace bytes rk_seg_build_tables needs for this batch. */
+rk_status rk_seg_tables_workspace_bytes(const rk_pool *pool, const rk_batch_desc *batch, size_t *bytes);
+
+/* Resolve head classes, compute every (layer, KV head, seq)'s held token ranges, expand them to
+ * pages, allocate the pages (all or nothing), build the dense logical->physical page tables and the
+ * balanced work schedule, and upload them into d_workspace on `stream`.
+ *   Held tokens: GLOBAL [0, kv_len); LOCAL [0, min(sink, kv_len)) and [max(0, q_start - window + 1),
+ *   kv_len), expanded to whole pages; runs that overlap or touch merge into one segment.
+ *   Allocation: pages are taken from the free list's head in ascending (layer, KV head, seq,
+ *   logical page) order.
+ * d_workspace: device, >= rk_seg_tables_workspace_bytes, 256-byte aligned, owned by the caller and
+ *   read by later device calls on these tables; it must outlive them.  NULL (with ws_bytes 0) builds
+ *   the tables on the host only: export, stats, trim and destroy work, device calls fail.
+ * Errors: RK_ERR_INVALID_ARG, RK_ERR_OUT_OF_PAGES (pool unchanged), RK_ERR_WORKSPACE_TOO_SMALL,
+ *   RK_ERR_HIP.  The host staging of the upload stays alive until the tables are destroyed. */
+rk_status rk_seg_build_tables(rk_pool *pool, const rk_batch_desc *batch, void *d_workspace,
+                              size_t ws_bytes, void *stream, rk_tables **out);
+
+/* Export the held segments and physical page ids of one (layer, KV head, seq), host side.
+ * seg_tok_begin / seg_npages: [seg_cap]; page_ids: [page_cap], in logical page order.
+ * *n_segs and *n_pages receive the full counts even when larger than the capacities. */
+rk_status rk_seg_tables_export(const rk_tables *tables, int32_t layer, int32_t kv_head, int32_t seq,
+                               int32_t *seg_tok_begin, int32_t *seg_npages, int32_t seg_cap,
+                               int32_t *n_segs, int32_t *page_ids, int32_t page_cap, int32_t *n_pages);
+
+/* Export the attention work schedule of one layer in launch order: items [cap][4] =
+ * (seq, kv_head, first query index within the sequence, number of key tiles visited). */
+rk_status rk_seg_tables_schedule(const rk_tables *tables, int32_t layer, int32_t *items, int64_t cap,
+                                 int64_t *n_items, int32_t *tokens_per_item, int32_t *key_tile);
+
+rk_status rk_seg_tables_stats(const rk_tables *tables, rk_tables_stats *out);
+
+/* After the call: LOCAL heads keep their sink pages and the pages covering
+ * [max(0, kv_len - window + 1), kv_len); every other LOCAL page returns to the free list (pushed on
+ * its head in ascending (layer, KV head, seq, logical page) order).  GLOBAL heads keep all pages.
+ * Afterwards the tables describe the retained state; device calls on them fail with RK_ERR_STATE. */
+rk_status rk_seg_tables_trim(rk_pool *pool, rk_tables *tables);
+
+/* Return every page the tables still hold to the free list (same order rule) and free the tables.
+ * Waits for the upload of the tables' host staging to finish. */
+rk_status rk_seg_tables_destroy(rk_pool *pool, rk_tables *tables);
+
+/* -- device calls -------------------------------------------------------------------------- */
+
+/* Position-independent reuse (page "RedKnot – 小红书研发并开源的长上下文大模型推理引擎", section
+ * RedKnot技术原理, 2. 位置无关缓存复用): import tokens [tok_begin, tok_begin + n_tok) of sequence `seq`
+ * into the held pages of every KV head of `layer`, rotating each key by delta = actual - offline
+ * position: pair m turns by delta * base^(-2m/D) (angle, cos and sin in fp64, rotation in fp32, one
+ * round-to-nearest-even store).  V is copied unchanged.  Tokens a head does not hold are skipped.
+ * src_k, src_v: device [num_kv_heads][n_tok][head_dim] with head stride src_head_stride elements
+ * (>= n_tok*head_dim); read only.  Requires tok_begin + n_tok <= kv_len[seq].
+ * Errors: RK_ERR_INVALID_ARG, RK_ERR_STATE (host-only or trimmed tables), RK_ERR_HIP. */
+rk_status rk_seg_reuse_rerotate(rk_pool *pool, const rk_tables *tables, int32_t layer, int32_t seq,
+                                int32_t tok_begin, int32_t n_tok, const void *src_k, const void *src_v,
+                                int64_t src_head_stride, int64_t delta, double rope_base,
+                                int32_t rope_style, void *stream);
+
+/* Write the query tokens' keys and values (k_new, v_new: [total_q][num_kv_heads][head_dim]) into
+ * their held pages of `layer` (the online KV cache write of EXECUTE, page "RedKnot -
+ * Xiaohongshuが開発した…", section 使い方). */
+rk_status rk_seg_append_kv(rk_pool *pool, const rk_tables *tables, int32_t layer, const void *k_new,
+                           const void *v_new, void *stream);
+
+/* EXECUTE's attention for one layer: append k_new / v_new (skipped when both are NULL, e.g. after
+ * rk_seg_append_kv), then mask-free head-ragged paged prefill attention.
+ * For every q head h and query token: o = sum over visible keys j of softmax_j(scale * q.k_j) v_j,
+ * lse = log sum exp(scale * q.k_j) over the same keys (fp32, natural log).
+ * q, o: [total_q][num_q_heads][head_dim]; lse: [num_q_heads][total_q] or NULL.
+ * softmax_scale <= 0 selects 1/sqrt(head_dim).  Accumulation and softmax are fp32; bf16 products
+ * run on the matrix cores; o is rounded once to the storage dtype.
+ * Errors: RK_ERR_INVALID_ARG, RK_ERR_STATE, RK_ERR_HIP. */
+rk_status rk_seg_attn_prefill(rk_pool *pool, const rk_tables *tables, int32_t layer, const void *q,
+                              const void *k_new, const void *v_new, void *o, float *lse,
+                              float softmax_scale, void *stream);
+
+/* -- diagnostics --------------------------------------------------------------------------- */
+
+const char *rk_status_string(rk_status s);
+const char *rk_last_error(void);
+/* Version string of the library build. */
+const char *rk_seg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RK_SEG_H */

@@ -85,3 +85,41 @@ def prefill(inp, scale: Optional[float] = None, rope_style: int = rope.ROTATE_HA
         o[cu[b]:cu[b + 1]] = ob.transpose(1, 0, 2)
         lse[:, cu[b]:cu[b + 1]] = lb
     return o, lse
+
+
+def head_kv(inp, seq: int, kv_head: int, rope_style: int = rope.ROTATE_HALF):
+    """Dense fp64 K, V [kv_len][D] of one (sequence, KV head): the slice of `sequence_kv` for that head."""
+    wl = inp.wl
+    L, qs = wl.kv_lens[seq], wl.q_starts[seq]
+    D = wl.head_dim
+    k = np.full((L, D), np.nan)
+    v = np.full((L, D), np.nan)
+    for doc in inp.docs:
+        if doc.seq != seq:
+            continue
+        sl = slice(doc.tok_begin, doc.tok_begin + doc.n_tok)
+        kk = rope.rotate(to64(doc.k_off[kv_head]), doc.delta, wl.rope_base, rope_style)
+        k[sl] = round_store(kk, wl.dtype)
+        v[sl] = to64(doc.v_off[kv_head])
+    cu = wl.cu_q()
+    k[qs:L] = to64(inp.k_new[cu[seq]:cu[seq + 1], kv_head])
+    v[qs:L] = to64(inp.v_new[cu[seq]:cu[seq + 1], kv_head])
+    if np.isnan(k).any() or np.isnan(v).any():
+        raise ValueError("sequence %d has prefix tokens that no reused document covers" % seq)
+    return k, v
+
+
+def prefill_rows(inp, seq: int, q_head: int, rows, scale: Optional[float] = None,
+                 rope_style: int = rope.ROTATE_HALF):
+    """o [n][D], lse [n] (fp64) of one q head for the given query rows of one sequence."""
+    wl = inp.wl
+    g = q_head // wl.group
+    k, v = head_kv(inp, seq, g, rope_style)
+    rows = np.asarray(rows, np.int64)
+    cu = wl.cu_q()
+    q = to64(inp.q[cu[seq] + torch.from_numpy(rows).to(inp.q.device), q_head])
+    if scale is None:
+        scale = 1.0 / np.sqrt(wl.head_dim)
+    cls = int(wl.head_class[wl.layer, g])
+    mask = attention.visibility_mask(cls, wl.q_starts[seq] + rows, wl.kv_lens[seq], wl.sink, wl.window)
+    return attention.masked_attention(q, k, v, mask, scale)

@@ -59,3 +59,19 @@ def test_reused_keys_equal_direct_rope_at_actual_position():
         np.testing.assert_allclose(k[:, d.tok_begin:d.tok_begin + d.n_tok], want, rtol=0, atol=2e-5)
         assert d.delta != 0
     np.testing.assert_array_equal(k[:, 64:], inp.k_new.double().numpy().transpose(1, 0, 2))
+
+
+def test_per_head_rows_equal_whole_call():
+    wl = workloads.random_small(5, torch.float32)
+    inp = workloads.make_inputs(wl)
+    o, lse = reference.prefill(inp)
+    cu = wl.cu_q()
+    for b in range(wl.num_seqs):
+        n = wl.q_lens[b]
+        if n == 0:
+            continue
+        rows = np.unique(np.array([0, n - 1, n // 2]))
+        for h in (0, wl.num_q_heads - 1):
+            ob, lb = reference.prefill_rows(inp, b, h, rows)
+            np.testing.assert_allclose(ob, o[cu[b] + rows, h], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lb, lse[h, cu[b] + rows], rtol=0, atol=1e-12)

@@ -166,9 +166,11 @@ def random_small(seed: int, dtype: torch.dtype = torch.bfloat16, allow_reuse: bo
     S = int(rng.choice([0, 1, 4, 17]))
     W = int(rng.choice([1, 16, 64, 100, 257, 1024]))
     hc = rng.integers(0, 2, size=(1, Hkv)).astype(np.uint8)
+    doc_len = int(rng.choice([0, 50, 200]))  # 0: the prefix is one document with delta 0 (chunked prefill)
     return Workload(name="random-small seed %d" % seed, config_id=100 + seed, num_layers=1, layer=0,
                     kv_lens=kv_lens, q_starts=q_starts, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
-                    page_size=P, sink=S, window=W, dtype=dtype, head_class=hc, pool_slack=7, doc_len=0)
+                    page_size=P, sink=S, window=W, dtype=dtype, head_class=hc, pool_slack=7, doc_len=doc_len,
+                    rope_base=float(rng.choice([1.0e4, 1.0e6])))
 
 
 # ----------------------------------------------------------------------------------------------
