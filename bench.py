@@ -1,0 +1,247 @@
+"""Benchmark of SegPagedAttention prefill on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input already resident in
+HBM: build the tables (resolve classes, held pages, allocation, schedule, upload), import reused
+documents with RoPE re-rotation (when the workload has any), append the new tokens' K/V, run the
+attention kernel, trim local heads to sink + window and release the tables.
+
+Default workload: the Llama-3.3-70B-shaped single-GPU share (31 sequences x 32K, 64 q / 8 KV heads,
+D=128, bf16, one global KV head, sink 4, window 2048, page 16).  The line also reports the same step
+with every head global (the dense reference), the 128K Qwen3-32B-shaped call, the attention
+kernel's roofline and the fp64 oracle's rate on a bounded sample of host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import workloads
+from head_aware_paged_prefill_amd import rk_seg
+from head_aware_paged_prefill_amd.runner import PrefillRunner
+
+METRIC = "SegPagedAttention prefill ms/layer & useful TFLOP/s at 32K/128K; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def useful_flops(stats: dict, head_dim: int) -> float:
+    """4 * D per visible (query, key) pair: QK^T and PV at 2 flops per multiply-add."""
+    return 4.0 * head_dim * stats["visible_pairs"]
+
+
+class Bench:
+    """Runs steps of one workload with inputs resident in HBM."""
+
+    def __init__(self, wl, inp, runner: PrefillRunner):
+        self.wl, self.inp, self.r = wl, inp, runner
+        self.o = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=wl.dtype, device="cuda")
+        self.lse = torch.empty((wl.num_q_heads, wl.total_q), dtype=torch.float32, device="cuda")
+        self.attn_ms, self.append_ms, self.import_ms = [], [], []
+        self.stats = None
+
+    def step(self, timed: bool) -> None:
+        wl, r = self.wl, self.r
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        r.build()
+        if timed:
+            ev[0].record()
+        r.import_docs(self.inp.docs)
+        if timed:
+            ev[1].record()
+        rk_seg.rk_seg_append_kv(r.tables, wl.layer, self.inp.k_new, self.inp.v_new)
+        if timed:
+            ev[2].record()
+        rk_seg.rk_seg_attn_prefill(r.tables, wl.layer, self.inp.q, None, None, self.o, self.lse)
+        if timed:
+            ev[3].record()
+        if self.stats is None:
+            self.stats = rk_seg.rk_seg_tables_stats(r.tables)
+        r.release(trim=True)
+        if timed:
+            self._pending = ev
+
+    def run(self, steps: int, warmup: int):
+        for _ in range(warmup):
+            self.step(False)
+        torch.cuda.synchronize()
+        evs = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(True)
+            evs.append(self._pending)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for e in evs:
+            self.import_ms.append(e[0].elapsed_time(e[1]))
+            self.append_ms.append(e[1].elapsed_time(e[2]))
+            self.attn_ms.append(e[2].elapsed_time(e[3]))
+        return (t1 - t0) * 1e3 / steps
+
+
+def run_workload(wl, steps: int, warmup: int, with_dense: bool):
+    log("workload: %s" % wl.name)
+    inp = workloads.make_inputs(wl, device="cuda")
+    runner = PrefillRunner(wl, free_order=inp.free_order, poison=True)
+    b = Bench(wl, inp, runner)
+    ms_step = b.run(steps, warmup)
+    flops = useful_flops(b.stats, wl.head_dim)
+    res = {
+        "ms_per_step": ms_step,
+        "ms_attention": float(np.mean(b.attn_ms)),
+        "ms_attention_min": float(np.min(b.attn_ms)),
+        "ms_append": float(np.mean(b.append_ms)),
+        "ms_import": float(np.mean(b.import_ms)),
+        "useful_tflop": flops / 1e12,
+        "visible_pairs": b.stats["visible_pairs"],
+        "key_tiles": b.stats["key_tiles"],
+        "work_items": b.stats["work_items"],
+        "pages_held": b.stats["pages_held"],
+    }
+    res["tflops_step"] = flops / (ms_step * 1e-3) / 1e12
+    res["tflops_attention"] = flops / (res["ms_attention"] * 1e-3) / 1e12
+    res["pct_mfma_peak_attention"] = 100.0 * res["tflops_attention"] / PEAK_BF16_TFLOPS
+    log("  mixed: %.3f ms/step, attention %.3f ms, %.1f useful TFLOP/s (%.1f%% of bf16 peak)" % (
+        ms_step, res["ms_attention"], res["tflops_attention"], res["pct_mfma_peak_attention"]))
+    if with_dense:
+        wl_d = wl.with_classes(np.ones_like(wl.head_class), wl.name + " all-global")
+        bd = Bench(wl_d, dataclasses.replace(inp, wl=wl_d), runner)
+        bd.r.wl = wl_d
+        ms_d = bd.run(max(1, steps // 2), 1)
+        runner.wl = wl
+        fd = useful_flops(bd.stats, wl.head_dim)
+        res["dense_reference"] = {
+            "ms_per_step": ms_d, "ms_attention": float(np.mean(bd.attn_ms)), "useful_tflop": fd / 1e12,
+            "tflops_attention": fd / (float(np.mean(bd.attn_ms)) * 1e-3) / 1e12,
+            "pct_mfma_peak_attention": 100.0 * fd / (float(np.mean(bd.attn_ms)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        }
+        res["dense_over_mixed_time"] = res["dense_reference"]["ms_attention"] / res["ms_attention"]
+        res["dense_over_mixed_pairs"] = fd / flops
+        log("  dense reference: attention %.3f ms, %.1f TFLOP/s (%.1f%%)" % (
+            res["dense_reference"]["ms_attention"], res["dense_reference"]["tflops_attention"],
+            res["dense_reference"]["pct_mfma_peak_attention"]))
+    runner.close()
+    del inp, b, runner
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(wl, budget_s: float = 15.0):
+    """The fp64 oracle on host cores, on a seeded sample of 256-row blocks of (sequence, q head)."""
+    from oracle import attention as oatt
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS defaults to every core it may run on
+        threads = len(os.sched_getaffinity(0))
+    rng = np.random.Generator(np.random.PCG64(99))
+    D = wl.head_dim
+    scale = 1.0 / np.sqrt(D)
+    done_flops, t_used, blocks = 0.0, 0.0, 0
+    cache = {}
+    while t_used < budget_s and blocks < 4096:
+        b = int(rng.integers(0, wl.num_seqs))
+        h = int(rng.integers(0, wl.num_q_heads))
+        L, qs = wl.kv_lens[b], wl.q_starts[b]
+        nq = L - qs
+        r0 = int(rng.integers(0, max(1, (nq + 255) // 256))) * 256
+        rows = np.arange(r0, min(nq, r0 + 256))
+        g = h // wl.group
+        key = (b, g)
+        if key not in cache:
+            cache.clear()
+            k = np.random.Generator(np.random.PCG64(b * 1000 + g)).standard_normal((L, D)).astype(np.float32)
+            v = np.random.Generator(np.random.PCG64(b * 1000 + g + 1)).standard_normal((L, D)).astype(np.float32)
+            cache[key] = (k.astype(np.float64), v.astype(np.float64))
+        k, v = cache[key]
+        q = np.random.Generator(np.random.PCG64(blocks)).standard_normal((len(rows), D))
+        cls = int(wl.head_class[wl.layer, g])
+        t0 = time.perf_counter()
+        mask = oatt.visibility_mask(cls, qs + rows, L, wl.sink, wl.window)
+        oatt.masked_attention(q, k, v, mask, scale)
+        t_used += time.perf_counter() - t0
+        done_flops += 4.0 * D * float(mask.sum())
+        blocks += 1
+    return {"value": done_flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d random 256-row blocks of (sequence, q head) of the workload (%.1f s of fp64 NumPy "
+                      "dense masked attention), useful flops only" % (blocks, t_used)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama70b", choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the dense reference and the 128K call")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (a known-size HBM reference for counters)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: the method's kernel runs on one GPU's share of the work and no "
+              "part of it is sharded or communicates; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    rk_seg.load()
+    if a.copy_mib > 0:
+        src = torch.empty(a.copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    wl = workloads.CONFIGS[a.workload]()
+    main_res = run_workload(wl, a.steps, a.warmup, with_dense=not a.no_extra)
+    extra = {}
+    if not a.no_extra and a.workload != "qwen32b":
+        extra["qwen32b_128k"] = run_workload(workloads.qwen32b(), max(2, a.steps // 2), 1, with_dense=True)
+    cpu = None if a.no_cpu else cpu_baseline(wl, a.cpu_seconds)
+    ms_attn = main_res["ms_attention"]
+    achieved = main_res["tflops_attention"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["tflops_step"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) inputs of the workload's shape (no dataset, no weights)",
+        "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "kv_lens": sorted(set(wl.kv_lens)),
+                   "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "page_size": wl.page_size, "sink": wl.sink, "window": wl.window,
+                   "global_kv_heads_in_layer": int(wl.head_class[wl.layer].sum())},
+        "ms_per_layer_attention": round(ms_attn, 4),
+        "useful_tflops_attention": round(achieved, 3),
+        "pct_mfma_peak_attention": round(main_res["pct_mfma_peak_attention"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "detail": main_res,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
