@@ -86,21 +86,36 @@ __device__ __forceinline__ bool visible(int cls, int i, int j, int sink, int win
 // bf16 attention
 // ------------------------------------------------------------------------------------------------
 
+constexpr int kAttnWaves = 8;                 // 2 waves per SIMD: one wave's softmax overlaps the other's MFMA
+constexpr int kAttnThreads = 64 * kAttnWaves;
+static_assert(kAttnWaves * 32 == kRowsPerItem, "one 32-query column block per wave");
+
 template <int D>
 struct AttnBf16Smem {
-  static constexpr int KP = D + 8;   // K row pitch (elements)
+  static constexpr int KP = D + 8;   // K row pitch (elements): +16 bytes spreads rows over all banks
   static constexpr int VP = BN + 8;  // V^T row pitch (elements)
   bf16_t k[2][BN * KP];
   bf16_t v[2][D * VP];
 };
 
+// max / sum of a value over the two half-waves (lanes l and l ^ 32)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) attn_bf16(AttnParams p) {
+__global__ void __launch_bounds__(kAttnThreads, 1) attn_bf16(AttnParams p) {
   constexpr int KP = AttnBf16Smem<D>::KP;
   constexpr int VP = AttnBf16Smem<D>::VP;
-  constexpr int NC = D / 16;           // 16-channel chunks of the QK product
-  constexpr int ND = D / 32;           // 32-channel blocks of O^T
-  constexpr int NLD = BN * D / 8 / kThreads;  // 16-byte chunks per thread per tile (K and V each)
+  constexpr int NC = D / 16;                       // 16-channel chunks of the QK product
+  constexpr int ND = D / 32;                       // 32-channel blocks of O^T
+  constexpr int NLD = BN * D / 8 / kAttnThreads;   // 16-byte chunks per thread per tile (K and V each)
+  static_assert(NLD >= 1, "tile too small for the workgroup");
   __shared__ __attribute__((aligned(16))) AttnBf16Smem<D> sm;
 
   const int tid = threadIdx.x;
@@ -113,109 +128,102 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16(AttnParams p) {
   const int L = si.kv_len;
   const TileRange tr = tile_range(cls, si.q_start + it.tok0, si.q_start + tok_end - 1, p.sink, p.window);
   const int ntiles = tr.count();
-  const int32_t *pt = p.page_ids + p.page_base[g * p.num_seqs + it.seq];
-  const bf16_t *kpg = static_cast<const bf16_t *>(p.k_pages);
-  const bf16_t *vpg = static_cast<const bf16_t *>(p.v_pages);
+  const int32_t *__restrict__ pt = p.page_ids + p.page_base[g * p.num_seqs + it.seq];
+  const bf16_t *__restrict__ kpg = static_cast<const bf16_t *>(p.k_pages);
+  const bf16_t *__restrict__ vpg = static_cast<const bf16_t *>(p.v_pages);
   const int P = p.P, log2P = p.log2P;
+  const int n_logical = (L + P - 1) >> log2P;
 
-  // ---- the two query rows (columns of S^T) this lane owns
-  int pos[2], tq[2], hq[2];
-  bool valid[2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int r = wave * 64 + n * 32 + m;
-    const int hh = r / p.T;
-    const int t = it.tok0 + (r - hh * p.T);
-    valid[n] = hh < p.G && t < tok_end;
-    pos[n] = valid[n] ? si.q_start + t : -1;
-    tq[n] = t;
-    hq[n] = g * p.G + hh;
-  }
-  const int wmin = wave_min(min(valid[0] ? pos[0] : INT32_MAX, valid[1] ? pos[1] : INT32_MAX));
-  const int wmax = wave_max(max(pos[0], pos[1]));
+  // ---- the query row (column of S^T) this lane owns
+  const int r = wave * 32 + m;
+  const int hh = r / p.T;
+  const int tq = it.tok0 + (r - hh * p.T);
+  const bool valid = hh < p.G && tq < tok_end;
+  const int pos = valid ? si.q_start + tq : -1;
+  const int hq = g * p.G + hh;
+  const int wmin = wave_min(valid ? pos : INT32_MAX);
+  const int wmax = wave_max(pos);
 
-  bf16x8 qf[2][NC];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const bf16_t *qrow = static_cast<const bf16_t *>(p.q) + ((int64_t)(si.cu_q + tq[n]) * p.H + hq[n]) * D;
+  bf16x8 qf[NC];
+  {
+    const bf16_t *qrow = static_cast<const bf16_t *>(p.q) + ((int64_t)(si.cu_q + tq) * p.H + hq) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       bf16x8 z = {};
-      qf[n][c] = valid[n] ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * c + 8 * hl) : z;
+      qf[c] = valid ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * c + 8 * hl) : z;
     }
   }
 
-  // ---- tile staging: global -> registers -> LDS
+  // ---- tile-invariant geometry of this thread's 16-byte chunks
+  int k_lds[NLD], k_row[NLD], k_col[NLD];
+  int v_lds[NLD], v_key[NLD], v_pi[NLD], v_goff[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int c = tid + kAttnThreads * u;
+    k_row[u] = c / (D / 8);
+    k_col[u] = (c % (D / 8)) * 8;
+    k_lds[u] = swap_bits23(k_row[u]) * KP + k_col[u];
+    int d, kof;
+    if (P <= BN) {
+      const int per_page = D * P / 8;
+      const int pi = c / per_page;
+      const int idx = c - pi * per_page;
+      d = idx / (P / 8);
+      kof = pi * P + (idx - d * (P / 8)) * 8;
+      v_pi[u] = pi;
+      v_goff[u] = idx * 8;
+    } else {
+      d = c >> 3;
+      kof = (c & 7) * 8;
+      v_pi[u] = 0;
+      v_goff[u] = d * P + kof;
+    }
+    v_key[u] = kof;
+    v_lds[u] = d * VP + kof;
+  }
+
   u32x4 kr[NLD], vr[NLD];
-  int ko[NLD], vo[NLD];
   auto load_tile = [&](int tile) {
     const int j0 = tile * BN;
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int c = tid + kThreads * u;
-      const int row = c / (D / 8), col = c - row * (D / 8);
-      const int j = j0 + row;
+      const int j = j0 + k_row[u];
+      const int lp = __builtin_amdgcn_readfirstlane(j >> log2P);  // uniform over the wave
+      const int pg = lp < n_logical ? pt[lp] : -1;
       u32x4 val = {0u, 0u, 0u, 0u};
-      if (j < L) {
-        const int pg = pt[j >> log2P];
-        if (pg >= 0)
-          val = *reinterpret_cast<const u32x4 *>(kpg + ((int64_t)pg * P + (j & (P - 1))) * D + col * 8);
-      }
+      if (pg >= 0 && j < L) val = *reinterpret_cast<const u32x4 *>(kpg + ((int64_t)pg * P + (j & (P - 1))) * D + k_col[u]);
       kr[u] = val;
-      ko[u] = swap_bits23(row) * KP + col * 8;
     }
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int c = tid + kThreads * u;
-      int d, kof, pg = -1;
-      int64_t src;
-      if (P <= BN) {
-        const int per_page = D * P / 8;
-        const int pi = c / per_page;
-        const int idx = c - pi * per_page;
-        d = idx / (P / 8);
-        kof = pi * P + (idx - d * (P / 8)) * 8;
-        const int j = j0 + kof;
-        if (j < L) pg = pt[j >> log2P];
-        src = (int64_t)pg * D * P + (int64_t)idx * 8;
-      } else {
-        d = c >> 3;
-        kof = (c & 7) * 8;
-        const int j = j0 + kof;
-        if (j < L) pg = pt[j >> log2P];
-        src = (int64_t)pg * D * P + (int64_t)d * P + (j & (P - 1));
-      }
-      const int j = j0 + kof;
+      const int j = j0 + v_key[u];
+      const int lp = __builtin_amdgcn_readfirstlane((j0 >> log2P) + v_pi[u]);
+      const int pg = lp < n_logical ? pt[lp] : -1;
       u32x4 val = {0u, 0u, 0u, 0u};
-      if (pg >= 0) {
-        val = *reinterpret_cast<const u32x4 *>(vpg + src);
+      if (pg >= 0 && j < L) {
+        const int64_t off = (int64_t)pg * D * P + v_goff[u] + (P > BN ? (j0 & (P - 1)) : 0);
+        val = *reinterpret_cast<const u32x4 *>(vpg + off);
         if (j + 8 > L) val = keep_first_bf16(val, L - j);
       }
       vr[u] = val;
-      vo[u] = d * VP + kof;
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      *reinterpret_cast<u32x4 *>(&sm.k[buf][ko[u]]) = kr[u];
-      *reinterpret_cast<u32x4 *>(&sm.v[buf][vo[u]]) = vr[u];
+      *reinterpret_cast<u32x4 *>(&sm.k[buf][k_lds[u]]) = kr[u];
+      *reinterpret_cast<u32x4 *>(&sm.v[buf][v_lds[u]]) = vr[u];
     }
   };
 
-  f32x16 oacc[2][ND];
+  f32x16 oacc[ND];
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[n][db] = f32x16{};
-  float mrun[2] = {kNegBig, kNegBig};
-  float lsum[2] = {0.f, 0.f};
+  for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
+  float mrun = kNegBig, lsum = 0.f;
   const float c2 = p.scale_log2;
 
-  if (ntiles > 0) {
-    load_tile(tr.tile(0));
-    store_tile(0);
-  }
+  load_tile(tr.tile(0));
+  store_tile(0);
   __syncthreads();
 
   for (int idx = 0; idx < ntiles; ++idx) {
@@ -230,84 +238,85 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16(AttnParams p) {
     if (!skip) {
       const bf16_t *Kb = sm.k[buf];
       const bf16_t *Vb = sm.v[buf];
+      // S^T for the tile's 64 keys (two 32-key blocks) x this wave's 32 queries
+      f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s[2] = {f32x16{}, f32x16{}};
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+        for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + (32 * kb + m) * KP + 16 * c + 8 * hl);
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][c], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][c], s[1], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
         }
-        bf16x8 pk[2][2];
+      if (!full) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          if (!full) {
-            const int jb = j0 + 32 * kb + 8 * hl;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = jb + 16 * (i >> 3) + (i & 7);
-              if (!visible(cls, pos[n], j, p.sink, p.window)) s[n][i] = -INFINITY;
-            }
-          }
-          float mt = s[n][0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[n][i]);
-          mt = fmaxf(mt, __shfl_xor(mt, 32));
-          const float mts = mt * c2;
-          if (__any(mts > mrun[n] + kRescaleSlack)) {
-            const float mnew = fmaxf(mrun[n], mts);
-            const float alpha = fast_exp2(mrun[n] - mnew);
-#pragma unroll
-            for (int db = 0; db < ND; ++db) oacc[n][db] *= alpha;
-            lsum[n] *= alpha;
-            mrun[n] = mnew;
-          }
-          f32x8 e0, e1;
-          float ps = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            e0[i] = fast_exp2(fmaf(s[n][i], c2, -mrun[n]));
-            e1[i] = fast_exp2(fmaf(s[n][i + 8], c2, -mrun[n]));
-            ps += e0[i] + e1[i];
-          }
-          lsum[n] += ps;
-          pk[n][0] = __builtin_convertvector(e0, bf16x8);
-          pk[n][1] = __builtin_convertvector(e1, bf16x8);
-        }
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8 *>(Vb + (32 * db + m) * VP + 32 * kb + 16 * cc + 8 * hl);
-            oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][cc], oacc[0][db], 0, 0, 0);
-            oacc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[1][cc], oacc[1][db], 0, 0, 0);
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + 32 * kb + 16 * (i >> 3) + 8 * hl + (i & 7);
+            if (!visible(cls, pos, j, p.sink, p.window)) s[kb][i] = -INFINITY;
           }
       }
+      float mt = s[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
+      mt = halves_max(mt);
+      const float mts = mt * c2;
+      if (__any(mts > mrun + kRescaleSlack)) {
+        const float mnew = fmaxf(mrun, mts);
+        const float alpha = fast_exp2(mrun - mnew);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+        lsum *= alpha;
+        mrun = mnew;
+      }
+      bf16x8 pk[2][2];
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x8 e0, e1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          e0[i] = fast_exp2(fmaf(s[kb][i], c2, -mrun));
+          e1[i] = fast_exp2(fmaf(s[kb][i + 8], c2, -mrun));
+          ps += e0[i] + e1[i];
+        }
+        pk[kb][0] = __builtin_convertvector(e0, bf16x8);
+        pk[kb][1] = __builtin_convertvector(e1, bf16x8);
+      }
+      lsum += ps;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int db = 0; db < ND; ++db) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8 *>(Vb + (32 * db + m) * VP + 32 * kb + 16 * cc + 8 * hl);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kb][cc], oacc[db], 0, 0, 0);
+          }
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: O^T accumulator (lane column = query, 16 channels per 32-channel block)
+  const float lt = halves_sum(lsum);
+  if (!valid) return;
+  const float inv = 1.0f / lt;
+  bf16_t *orow = static_cast<bf16_t *>(p.o) + ((int64_t)(si.cu_q + tq) * p.H + hq) * D;
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const float lt = lsum[n] + __shfl_xor(lsum[n], 32);
-    if (!valid[n]) continue;
-    const float inv = 1.0f / lt;
-    bf16_t *orow = static_cast<bf16_t *>(p.o) + ((int64_t)(si.cu_q + tq[n]) * p.H + hq[n]) * D;
+  for (int db = 0; db < ND; ++db)
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        f32x4 w = {oacc[n][db][4 * a4 + 0] * inv, oacc[n][db][4 * a4 + 1] * inv, oacc[n][db][4 * a4 + 2] * inv,
-                   oacc[n][db][4 * a4 + 3] * inv};
-        *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * a4 + 4 * hl) = __builtin_convertvector(w, bf16x4);
-      }
-    if (p.lse && hl == 0)
-      p.lse[(int64_t)hq[n] * p.total_q + si.cu_q + tq[n]] = (mrun[n] + log2f(lt)) * 0.69314718055994531f;
-  }
+    for (int a4 = 0; a4 < 4; ++a4) {
+      f32x4 w = {oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
+                 oacc[db][4 * a4 + 3] * inv};
+      *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * a4 + 4 * hl) = __builtin_convertvector(w, bf16x4);
+    }
+  if (p.lse && hl == 0)
+    p.lse[(int64_t)hq * p.total_q + si.cu_q + tq] = (mrun + log2f(lt)) * 0.69314718055994531f;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -538,9 +547,9 @@ hipError_t launch_attention(const AttnParams &p, int dtype, int head_dim, hipStr
   dim3 grid(p.n_items);
   if (dtype == RK_BF16) {
     if (head_dim == 128)
-      hipLaunchKernelGGL(attn_bf16<128>, grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL(attn_bf16<128>, grid, dim3(kAttnThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL(attn_bf16<64>, grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL(attn_bf16<64>, grid, dim3(kAttnThreads), 0, stream, p);
   } else {
     if (head_dim == 128)
       hipLaunchKernelGGL(attn_f32<128>, grid, dim3(kF32Threads), 0, stream, p);
