@@ -93,7 +93,7 @@ static_assert(kAttnWaves * 32 == kRowsPerItem, "one 32-query column block per wa
 template <int D>
 struct AttnBf16Smem {
   static constexpr int KP = D + 8;   // K row pitch (elements): +16 bytes spreads rows over all banks
-  static constexpr int VP = BN + 8;  // V^T row pitch (elements)
+  static constexpr int VP = BN + 8;  // V^T row pitch (elements), same reason
   bf16_t k[2][BN * KP];
   bf16_t v[2][D * VP];
 };
@@ -115,11 +115,14 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_bf16(AttnParams p) {
   constexpr int NC = D / 16;                       // 16-channel chunks of the QK product
   constexpr int ND = D / 32;                       // 32-channel blocks of O^T
   constexpr int NLD = BN * D / 8 / kAttnThreads;   // 16-byte chunks per thread per tile (K and V each)
+  constexpr int ROWS_PER_WAVE_LD = 64 * 8 / D;     // K rows one wave-wide chunk load covers
   static_assert(NLD >= 1, "tile too small for the workgroup");
   __shared__ __attribute__((aligned(16))) AttnBf16Smem<D> sm;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, m = lane & 31;
+  // the wave index is uniform: keep it (and everything derived from it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hl = lane >> 5, m = lane & 31;
   const Item it = p.items[blockIdx.x];
   const SeqInfo si = p.seqs[it.seq];
   const int g = it.kv_head;
@@ -133,6 +136,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_bf16(AttnParams p) {
   const bf16_t *__restrict__ vpg = static_cast<const bf16_t *>(p.v_pages);
   const int P = p.P, log2P = p.log2P;
   const int n_logical = (L + P - 1) >> log2P;
+  const int64_t page_elems = (int64_t)P * D;
 
   // ---- the query row (column of S^T) this lane owns
   const int r = wave * 32 + m;
@@ -141,8 +145,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_bf16(AttnParams p) {
   const bool valid = hh < p.G && tq < tok_end;
   const int pos = valid ? si.q_start + tq : -1;
   const int hq = g * p.G + hh;
-  const int wmin = wave_min(valid ? pos : INT32_MAX);
-  const int wmax = wave_max(pos);
+  // wave-uniform query range: scalar registers, so tile classes are scalar branches
+  const int wmin = __builtin_amdgcn_readfirstlane(wave_min(valid ? pos : INT32_MAX));
+  const int wmax = __builtin_amdgcn_readfirstlane(wave_max(pos));
 
   bf16x8 qf[NC];
   {
@@ -154,15 +159,16 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_bf16(AttnParams p) {
     }
   }
 
-  // ---- tile-invariant geometry of this thread's 16-byte chunks
-  int k_lds[NLD], k_row[NLD], k_col[NLD];
-  int v_lds[NLD], v_key[NLD], v_pi[NLD], v_goff[NLD];
+  // ---- tile-invariant geometry of this thread's 16-byte chunks.  Chunk u of a wave covers a
+  // contiguous kilobyte of one page: a scalar page base plus lane * 16 bytes.
+  int k_lds[NLD], v_lds[NLD], v_key[NLD];
+  int k_row0[NLD], v_pi[NLD], v_goff0[NLD];  // wave-uniform parts
 #pragma unroll
   for (int u = 0; u < NLD; ++u) {
     const int c = tid + kAttnThreads * u;
-    k_row[u] = c / (D / 8);
-    k_col[u] = (c % (D / 8)) * 8;
-    k_lds[u] = swap_bits23(k_row[u]) * KP + k_col[u];
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    k_lds[u] = swap_bits23(row) * KP + col;
+    k_row0[u] = (wave * 64 + kAttnThreads * u) / (D / 8);
     int d, kof;
     if (P <= BN) {
       const int per_page = D * P / 8;
@@ -170,40 +176,49 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_bf16(AttnParams p) {
       const int idx = c - pi * per_page;
       d = idx / (P / 8);
       kof = pi * P + (idx - d * (P / 8)) * 8;
-      v_pi[u] = pi;
-      v_goff[u] = idx * 8;
+      v_pi[u] = (wave * 64 + kAttnThreads * u) / per_page;  // == pi: a wave's 64 chunks share one page
+      v_goff0[u] = ((wave * 64 + kAttnThreads * u) - v_pi[u] * per_page) * 8;  // + lane * 8
     } else {
       d = c >> 3;
       kof = (c & 7) * 8;
       v_pi[u] = 0;
-      v_goff[u] = d * P + kof;
+      v_goff0[u] = ((wave * 64 + kAttnThreads * u) >> 3) * P;  // + (lane >> 3) * P + (lane & 7) * 8
     }
     v_key[u] = kof;
     v_lds[u] = d * VP + kof;
   }
+  const int v_lane_off = P <= BN ? lane * 8 : (lane >> 3) * P + (lane & 7) * 8;
 
   u32x4 kr[NLD], vr[NLD];
   auto load_tile = [&](int tile) {
     const int j0 = tile * BN;
+    const bool tail = j0 + BN > L;
+    // page ids first (scalar loads, all in flight together), then the 16-byte data loads
+    int pgk[NLD], pgv[NLD];
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int j = j0 + k_row[u];
-      const int lp = __builtin_amdgcn_readfirstlane(j >> log2P);  // uniform over the wave
-      const int pg = lp < n_logical ? pt[lp] : -1;
+      const int lk = (j0 + k_row0[u]) >> log2P;
+      const int lv = (j0 >> log2P) + v_pi[u];
+      pgk[u] = lk < n_logical ? pt[lk] : -1;
+      pgv[u] = lv < n_logical ? pt[lv] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int jw = j0 + k_row0[u];  // first key of the wave's kilobyte
       u32x4 val = {0u, 0u, 0u, 0u};
-      if (pg >= 0 && j < L) val = *reinterpret_cast<const u32x4 *>(kpg + ((int64_t)pg * P + (j & (P - 1))) * D + k_col[u]);
+      const bf16_t *src = kpg + (int64_t)pgk[u] * page_elems + (int64_t)(jw & (P - 1)) * D + lane * 8;
+      if (pgk[u] >= 0 && (!tail || jw + lane / (D / 8) < L)) val = *reinterpret_cast<const u32x4 *>(src);
       kr[u] = val;
     }
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int j = j0 + v_key[u];
-      const int lp = __builtin_amdgcn_readfirstlane((j0 >> log2P) + v_pi[u]);
-      const int pg = lp < n_logical ? pt[lp] : -1;
       u32x4 val = {0u, 0u, 0u, 0u};
-      if (pg >= 0 && j < L) {
-        const int64_t off = (int64_t)pg * D * P + v_goff[u] + (P > BN ? (j0 & (P - 1)) : 0);
-        val = *reinterpret_cast<const u32x4 *>(vpg + off);
-        if (j + 8 > L) val = keep_first_bf16(val, L - j);
+      const bf16_t *src =
+          vpg + (int64_t)pgv[u] * page_elems + v_goff0[u] + (P > BN ? (j0 & (P - 1)) : 0) + v_lane_off;
+      const int j = j0 + v_key[u];
+      if (pgv[u] >= 0 && (!tail || j < L)) {
+        val = *reinterpret_cast<const u32x4 *>(src);
+        if (tail && j + 8 > L) val = keep_first_bf16(val, L - j);
       }
       vr[u] = val;
     }
@@ -221,6 +236,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_bf16(AttnParams p) {
   for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
   float mrun = kNegBig, lsum = 0.f;
   const float c2 = p.scale_log2;
+  const int win_lo = cls == RK_GLOBAL ? 0 : pos - p.window + 1;  // first window key of this row
 
   load_tile(tr.tile(0));
   store_tile(0);
@@ -248,13 +264,27 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_bf16(AttnParams p) {
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
         }
       if (!full) {
+        // key of register i of block kb: jb + 16 * (i / 8) + i % 8, jb = j0 + 32 kb + 8 hl
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          const int jb = j0 + 32 * kb + 8 * hl;
+          const int hi = pos - jb;     // visible: off <= hi
+          const int lo = win_lo - jb;  // local: off >= lo, or off < sk
+          const int sk = p.sink - jb;
+          if (cls == RK_GLOBAL) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = j0 + 32 * kb + 16 * (i >> 3) + 8 * hl + (i & 7);
-            if (!visible(cls, pos, j, p.sink, p.window)) s[kb][i] = -INFINITY;
+            for (int i = 0; i < 16; ++i) {
+              const int off = 16 * (i >> 3) + (i & 7);
+              s[kb][i] = off <= hi ? s[kb][i] : -INFINITY;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int off = 16 * (i >> 3) + (i & 7);
+              s[kb][i] = (off <= hi && (off >= lo || off < sk)) ? s[kb][i] : -INFINITY;
+            }
           }
+        }
       }
       float mt = s[0][0];
 #pragma unroll
