@@ -37,7 +37,9 @@
  * token is below kv_len must have been written -- by the append inside
  * rk_seg_attn_prefill (tokens >= q_start) or by rk_seg_reuse_rerotate (tokens
  * below q_start).  Slots at or beyond kv_len and pages a head does not hold may
- * contain any bits (NaN included); they never reach the output.
+ * contain any bits (NaN included) before the call; the append clears the slots
+ * of a sequence's last page past kv_len, and pages a head does not hold are
+ * never read.  None of them reaches the output.
  *
  * Errors: every call returns an rk_status; no exception crosses the ABI.  On
  * failure, rk_last_error() returns a thread-local message.  A failed call
@@ -203,7 +205,9 @@ rk_status rk_seg_reuse_rerotate(rk_pool *pool, const rk_tables *tables, int32_t 
 
 /* Write the query tokens' keys and values (k_new, v_new: [total_q][num_kv_heads][head_dim]) into
  * their held pages of `layer` (the online KV cache write of EXECUTE, page "RedKnot -
- * Xiaohongshuが開発した…", section 使い方). */
+ * Xiaohongshuが開発した…", section 使い方), and set the slots past kv_len of each sequence's last
+ * page to zero.  Attention on these tables requires this call (or the append inside
+ * rk_seg_attn_prefill) to have run. */
 rk_status rk_seg_append_kv(rk_pool *pool, const rk_tables *tables, int32_t layer, const void *k_new,
                            const void *v_new, void *stream);
 
