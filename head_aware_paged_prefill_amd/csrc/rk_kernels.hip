@@ -147,6 +147,7 @@ __global__ void __launch_bounds__(kRowsPerItem / NB * 2, 1) attn_bf16(AttnParams
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hl = lane >> 5, m = lane & 31;
   const Item it = p.items[blockIdx.x];
+  if (it.seq < 0) return;  // schedule padding: keeps the next items on their XCD
   const SeqInfo si = p.seqs[it.seq];
   const int g = it.kv_head;
   const int cls = p.head_class[g];
@@ -455,6 +456,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp(AttnParams p) {
   const int group = RK_PP_GROUP_SHIFT == 2 ? (wave >> 2) : (wave & 1);
   const int lane = tid & 63, hl = lane >> 5, m = lane & 31;
   const Item it = p.items[blockIdx.x];
+  if (it.seq < 0) return;  // schedule padding: keeps the next items on their XCD
   const SeqInfo si = p.seqs[it.seq];
   const int g = it.kv_head;
   const int cls = p.head_class[g];
@@ -723,6 +725,7 @@ __global__ void __launch_bounds__(kF32Threads, 1) attn_f32(AttnParams p) {
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5;
   const int r = wave * 32 + (lane & 31);
   const Item it = p.items[blockIdx.x];
+  if (it.seq < 0) return;  // schedule padding: keeps the next items on their XCD
   const SeqInfo si = p.seqs[it.seq];
   const int g = it.kv_head;
   const int cls = p.head_class[g];

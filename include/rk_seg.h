@@ -172,7 +172,9 @@ rk_status rk_seg_tables_export(const rk_tables *tables, int32_t layer, int32_t k
                                int32_t *n_segs, int32_t *page_ids, int32_t page_cap, int32_t *n_pages);
 
 /* Export the attention work schedule of one layer in launch order: items [cap][4] =
- * (seq, kv_head, first query index within the sequence, number of key tiles visited). */
+ * (seq, kv_head, first query index within the sequence, number of key tiles visited).  Workgroup i
+ * of the launch runs on XCD i % 8; entries with seq = -1 are empty slots that keep the next items
+ * on their XCD.  Every (seq, kv_head, q tile) appears exactly once. */
 rk_status rk_seg_tables_schedule(const rk_tables *tables, int32_t layer, int32_t *items, int64_t cap,
                                  int64_t *n_items, int32_t *tokens_per_item, int32_t *key_tile);
 

@@ -137,9 +137,16 @@ def test_schedule_covers_every_tile_once_and_visits_exactly_the_visible_tiles(se
     for l in range(c["lb"], c["le"]):
         items, T, BN = rk_seg.rk_seg_tables_schedule(t, l)
         assert T == 256 // c["G"] and BN == 64
-        assert all(items[i, 3] >= items[i + 1, 3] for i in range(len(items) - 1))  # longest first
+        # launch slot i runs on XCD i % 8: each XCD's slots run longest first
+        for x in range(8):
+            mine = [it for it in items[x::8].tolist() if it[0] >= 0]
+            assert all(mine[i][3] >= mine[i + 1][3] for i in range(len(mine) - 1))
+        assert len(items) == 0 or items[-1, 0] >= 0
         seen = set()
         for b_, g_, tok0, tiles in items.tolist():
+            if b_ < 0:
+                assert tiles == 0
+                continue
             assert (b_, g_, tok0) not in seen
             seen.add((b_, g_, tok0))
             q, L = c["qs"][b_], c["kv"][b_]
@@ -232,5 +239,34 @@ def test_empty_batch_and_zero_query_sequences():
     assert st["work_items"] == 0 and st["total_q"] == 0
     # the local head still holds sink + window for a next query: tokens [0,4) and [23,30) -> pages 0, 1
     assert rk_seg.rk_seg_tables_export(t, 0, 1, 0)[0] == [(0, 2, 0)]
+    rk_seg.rk_seg_tables_destroy(t)
+    rk_seg.rk_seg_pool_destroy(pool)
+
+
+def test_xcd_binned_schedule_on_the_31x32k_shape():
+    """31 x 32K, 1 global KV head of 8: global-head K/V (~500 MB) overflows the shared cache, so the
+    schedule bins work per XCD.  Coverage stays exact and the XCDs get near-equal key-tile totals."""
+    wl = workloads.llama70b()
+    N = sum(wl.num_kv_heads * (L // wl.page_size) for L in wl.kv_lens)
+    pool = fake_pool(N, None, 1, wl.num_kv_heads, 128, wl.page_size)
+    t = rk_seg.rk_seg_build_tables(pool, 0, 1, wl.num_q_heads, wl.q_starts, wl.kv_lens, wl.head_class, wl.sink,
+                                   wl.window, device=False)
+    items, T, BN = rk_seg.rk_seg_tables_schedule(t, 0)
+    real = items[items[:, 0] >= 0]
+    assert len(real) == 31 * 8 * (32768 // T)
+    assert len({(a, b, c) for a, b, c, _ in real.tolist()}) == len(real)
+    load = np.zeros(8)
+    for x in range(8):
+        mine = items[x::8]
+        mine = mine[mine[:, 0] >= 0]
+        assert (np.diff(mine[:, 3]) <= 0).all()
+        load[x] = mine[:, 3].sum()
+    assert load.max() / load.mean() < 1.05
+    # costs of a few items against the dense mask
+    rng = np.random.Generator(np.random.PCG64(5))
+    for b_, g_, tok0, tiles in real[rng.choice(len(real), 12, replace=False)].tolist():
+        pos = np.arange(tok0, tok0 + T)
+        m = attention.visibility_mask(int(wl.head_class[0, g_]), pos, 32768, wl.sink, wl.window)
+        assert tiles == len(set((np.flatnonzero(m.any(axis=0)) // BN).tolist()))
     rk_seg.rk_seg_tables_destroy(t)
     rk_seg.rk_seg_pool_destroy(pool)
