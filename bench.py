@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import dataclasses
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +32,26 @@ from head_aware_paged_prefill_amd.runner import PrefillRunner
 METRIC = "SegPagedAttention prefill ms/layer & useful TFLOP/s at 32K/128K; % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = {"llama70b": "attn_bf16_llama70b_31x32K_traffic.txt", "qwen32b": "attn_bf16_qwen32b_128K_traffic.txt"}
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
+    or None when there is none for this workload or the kernel sources changed since it was taken."""
+    name = PROFILES.get(workload)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
+        return None
+    kv = dict(line.strip().split("=", 1) for line in open(path) if "=" in line and not line.startswith(" "))
+    h = hashlib.sha256()
+    for f in kv.get("kernel_sources", "").split(","):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != kv.get("kernel_sources_sha256"):
+        return None
+    return int(kv["traffic_bytes_per_launch"])
 
 
 def log(msg: str) -> None:
@@ -235,7 +256,7 @@ def main():
         "useful_tflops_attention": round(achieved, 3),
         "pct_mfma_peak_attention": round(main_res["pct_mfma_peak_attention"], 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(a.workload)},
         "cpu_baseline": cpu,
         "detail": main_res,
         "extra": extra,
