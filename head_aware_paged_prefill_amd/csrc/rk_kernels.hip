@@ -11,20 +11,23 @@
 //    their offline to their actual position (page "RedKnot – 小红书研发并开源的长上下文大模型推理引擎"
 //    (shshi.cn), section RedKnot技术原理, 2. 位置无关缓存复用).
 //
-// Design of attn_bf16 (one work item = 256 query rows = G heads x T tokens of one KV head; 4 waves;
-// each wave owns 64 rows as two 32-column blocks):
+// Design of attn_bf16 (one work item = 256 query rows = G heads x T tokens of one KV head; eight
+// waves of 32 rows, two per SIMD):
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: keys are the M dimension, queries the N dimension, so
-//    each lane holds one query column and 16 keys per 32x32 block; a row max is 15 in-lane max ops
-//    plus one swap between the two half-waves.
-//  * K rows are written to LDS in a permuted order (bits 2 and 3 of the key index swapped) so that
-//    the S^T accumulator register i of lane half h holds key 16*(i/8) + 8*h + i%8: the eight
-//    probabilities a lane needs as the B operand of the PV product (O^T = V^T P^T) for 16-key chunk
-//    c are exactly its registers 8c..8c+7, converted to bf16 in place -- no shuffles.
+//    each lane holds one query column and 16 keys per 32x32 block; a row max is in-lane max3 ops
+//    plus one v_permlane32_swap between the two half-waves.
+//  * K rows sit in LDS in a permuted order (bits 2 and 3 of the key index swapped) so that the S^T
+//    accumulator register i of lane half h holds key 16*(i/8) + 8*h + i%8: the eight probabilities
+//    a lane needs as the B operand of the PV product (O^T = V^T P^T) for 16-key chunk c are
+//    exactly its registers 8c..8c+7, converted to bf16 in place -- no shuffles.
 //  * V pages are stored channel-major ([D][P]) so the A operand of PV (8 consecutive keys of one
-//    channel) is one 16-byte LDS read.  LDS rows are padded by 16 bytes to spread 16-byte reads
-//    over all banks.
-//  * K/V tiles of 64 keys are double-buffered in LDS; the next tile's global loads are issued
-//    before the current tile's MFMA work and written to LDS after it (one barrier per tile).
+//    channel) is one 16-byte LDS read.
+//  * Tiles reach LDS by direct global->LDS 16-byte loads (scalar page address + 32-bit lane
+//    offset), one 1 KB block per instruction; XOR swizzles of the 16-byte chunks keep the operand
+//    reads free of bank conflicts.
+//  * Two 64-key tiles per step, double-buffered: the next step's loads are issued before this
+//    step's MFMA work; one barrier per step.  The buffer index is a compile-time constant (the step
+//    loop is unrolled by two), so operand addresses are lane registers plus immediate offsets.
 //  * Online softmax in fp32 with exp2; the running max is only raised when a new score exceeds
 //    it by more than 2^8 in the exp2 domain, so the O rescale (64 VALU ops per block) is rare.
 //    Skipping it is exact: weights up to 2^8 are represented the same way in fp32 and bf16.
@@ -50,6 +53,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BN = kKeyTile;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest un-normalised weight allowed
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 __device__ __forceinline__ int swap_bits23(int j) { return (j & ~0xC) | ((j & 4) << 1) | ((j & 8) >> 1); }
 
@@ -86,8 +94,8 @@ __device__ __forceinline__ bool visible(int cls, int i, int j, int sink, int win
 // bf16 attention
 // ------------------------------------------------------------------------------------------------
 
-#ifndef RK_ATTN_NB
-#define RK_ATTN_NB 1
+#ifndef RK_TILES_PER_STEP
+#define RK_TILES_PER_STEP 2  // key tiles staged per LDS buffer and barrier step
 #endif
 
 // LDS image of one 64-key tile, filled by direct global->LDS 16-byte loads (lane l of a load
@@ -99,10 +107,10 @@ __device__ __forceinline__ bool visible(int cls, int i, int j, int sink, int win
 //     c ^ vswz(d).
 // Both swizzles make 16 consecutive lanes reading 16 consecutive rows at one chunk index touch 16
 // distinct 16-byte slots of every 256-byte bank window.
-template <int D>
+template <int D, int TPS>
 struct AttnBf16Smem {
-  bf16_t k[2][BN * D];  // double buffer: the next tile loads while this one is used
-  bf16_t v[2][D * BN];
+  bf16_t k[2][TPS][BN * D];  // double buffer: the next step's tiles load while these are used
+  bf16_t v[2][TPS][D * BN];
 };
 
 template <int D>
@@ -123,24 +131,35 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The value unchanged, hidden from code motion: a loop-invariant 32-bit lane offset then stays
+// 32-bit at its use, where it forms the scalar-base + 32-bit-offset address of a global load
+// (instead of a hoisted 64-bit vector address that holds two registers for the whole loop).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_block) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
                                    (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
 }
 
-// NB = 32-query column blocks per wave.  Every 16-byte K or V fragment read from LDS feeds NB
-// MFMAs, so LDS read traffic per flop falls as 1/NB; registers grow with NB (NB = 2 runs one wave
-// per SIMD).
-template <int D, int NB>
-__global__ void __launch_bounds__(kRowsPerItem / NB * 2, 1) attn_bf16(AttnParams p) {
-  constexpr int NWAVES = kRowsPerItem / (32 * NB);
+// One work item = 256 query rows; eight waves of 32 rows (one query column of S^T per lane).
+// Each step stages TPS key tiles of 64 keys (K and V) in one of two LDS buffers while the other
+// buffer's tiles are used: the loads of step s + 1 are issued before the compute of step s and one
+// barrier closes the step.  Per tile: S^T = K Q^T (16 MFMAs), the online softmax, O^T += V^T P^T
+// (16 MFMAs).
+// SMALLP: 8-key pages, where one 1 KB load block spans two pages.
+template <int D, bool SMALLP>
+__global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
   constexpr int NC = D / 16;                 // 16-channel chunks of the QK product
   constexpr int ND = D / 32;                 // 32-channel blocks of O^T
   constexpr int UNITS = BN * D * 2 / 1024;   // 1 KB load blocks per tile, for K and for V each
-  constexpr int NU = UNITS / NWAVES;         // per wave
+  constexpr int NU = UNITS / 8;              // per wave
   constexpr int KROWS_U = 512 / D;           // K rows per block
-  static_assert(NU >= 1 && UNITS % NWAVES == 0, "tile does not split over the waves");
-  __shared__ __attribute__((aligned(1024))) AttnBf16Smem<D> sm;
+  constexpr int TPS = RK_TILES_PER_STEP;
+  static_assert(NU >= 1 && UNITS % 8 == 0, "tile does not split over the waves");
+  __shared__ __attribute__((aligned(1024))) AttnBf16Smem<D, TPS> sm;
 
   const int tid = threadIdx.x;
   // the wave index is uniform: keep it (and everything derived from it) in scalar registers
@@ -155,7 +174,8 @@ __global__ void __launch_bounds__(kRowsPerItem / NB * 2, 1) attn_bf16(AttnParams
   const int L = si.kv_len;
   const int i_max = si.q_start + tok_end - 1;
   const TileRange tr = tile_range(cls, si.q_start + it.tok0, i_max, p.sink, p.window);
-  const int ntiles = tr.count();
+  const int ntiles = tr.count();  // >= 1
+  const int nsteps = (ntiles + TPS - 1) / TPS;
   const int32_t *__restrict__ pt = p.page_ids + p.page_base[g * p.num_seqs + it.seq];
   const bf16_t *__restrict__ kpg = static_cast<const bf16_t *>(p.k_pages);
   const bf16_t *__restrict__ vpg = static_cast<const bf16_t *>(p.v_pages);
@@ -168,312 +188,6 @@ __global__ void __launch_bounds__(kRowsPerItem / NB * 2, 1) attn_bf16(AttnParams
   // clears its slots past kv_len).  Its keys are masked out, so only finiteness matters.
   const int pg_fallback = pt[i_max >> log2P];
 
-  // ---- the NB query rows (columns of S^T) this lane owns
-  int pos[NB], tq[NB], hq[NB], win_lo[NB];
-  bool valid[NB];
-  int vmin = INT32_MAX, vmax = -1;
-#pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    const int r = wave * 32 * NB + 32 * n + m;
-    const int hh = r / p.T;
-    tq[n] = it.tok0 + (r - hh * p.T);
-    valid[n] = hh < p.G && tq[n] < tok_end;
-    pos[n] = valid[n] ? si.q_start + tq[n] : -1;
-    hq[n] = g * p.G + hh;
-    win_lo[n] = cls == RK_GLOBAL ? 0 : pos[n] - p.window + 1;  // first window key of the row
-    vmin = min(vmin, valid[n] ? pos[n] : INT32_MAX);
-    vmax = max(vmax, pos[n]);
-  }
-  // wave-uniform query range: scalar registers, so tile classes are scalar branches
-  const int wmin = __builtin_amdgcn_readfirstlane(wave_min(vmin));
-  const int wmax = __builtin_amdgcn_readfirstlane(wave_max(vmax));
-
-  bf16x8 qf[NB][NC];
-#pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    const bf16_t *qrow = static_cast<const bf16_t *>(p.q) + ((int64_t)(si.cu_q + tq[n]) * p.H + hq[n]) * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      bf16x8 z = {};
-      qf[n][c] = valid[n] ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * c + 8 * hl) : z;
-    }
-  }
-
-  // ---- tile-invariant geometry of this wave's 1 KB load blocks (block b = wave * NU + u)
-  int k_key0[NU], k_loff[NU];      // K: first key of the block (uniform); lane's element offset in its page
-  int v_pi[NU], v_loff[NU];        // V: page-in-tile (uniform); lane's element offset in its page
-  // a D = 64 K block spans 8 keys; with 8-key pages its two 4-key halves come from two pages
-  const bool k_split = D == 64 && P < 16;
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int b = wave * NU + u;
-    // K: LDS rows b*KROWS_U + lane/(D/8), slot lane % (D/8)
-    const int row = b * KROWS_U + lane / (D / 8);
-    const int slot = lane % (D / 8);
-    const int key = swap_bits23(row);
-    const int chunk = slot ^ kswz<D>(row);
-    k_key0[u] = swap_bits23(b * KROWS_U) & ~(KROWS_U - 1);
-    // pages of up to 64 keys: the tile starts on a page boundary; larger pages: + tile offset per tile
-    k_loff[u] = (P <= BN ? (key & (P - 1)) : key) * D + chunk * 8;
-    // V: block b of the [page][D][Pt] image
-    const int upp = D * Pt * 2 / 1024;  // blocks per page-in-tile image (>= 1 for Pt >= 8 with D >= 64)
-    const int pi = b / upp;
-    const int rows_u = 512 / Pt;        // channel rows per block
-    const int d = (b % upp) * rows_u + lane / (Pt / 8);
-    const int cl = lane % (Pt / 8);
-    const int cg = cl ^ vswz(d, Pt);
-    v_pi[u] = pi;
-    v_loff[u] = d * P + cg * 8;         // + (j0 & (P - 1)) when P > 64
-  }
-  // V^T read offsets (elements) for the four (kb, cc) key chunks of a 64-key tile, channel row m
-  int v_rd[4];
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const int k8 = 2 * q4 + hl;  // 8-key chunk 4kb + 2cc + hl
-    const int cpr = Pt / 8;
-    v_rd[q4] = (k8 / cpr) * D * Pt + m * Pt + (((k8 % cpr) ^ vswz(m, Pt)) << 3);
-  }
-  // K read offsets (elements) for the NC channel chunks, rows m (+32 for the second key block)
-  int k_rd[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) k_rd[c] = m * D + (((2 * c + hl) ^ kswz<D>(m)) << 3);
-
-  // Page ids of a tile: one vector load per wave (lane i < 64 / P holds the id of the tile's i-th
-  // page), issued a tile ahead and read back with readlane, so the lookup latency stays off the
-  // critical path and no scalar load shares the LDS wait counter with the operand reads.
-  const int npt = P < BN ? BN / P : 1;
-  auto load_ids = [&](int tile) -> int {
-    const int lp = ((tile * BN) >> log2P) + lane;
-    int v = -1;
-    if (lane < npt && lp < n_logical) v = pt[lp];
-    return v;
-  };
-  auto fix = [&](int pg) { return pg >= 0 ? pg : pg_fallback; };
-  auto issue_tile = [&](int tile, int buf, int ids) {
-    const int j0 = tile * BN;
-    int pgk[NU], pgv[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      pgk[u] = fix(__builtin_amdgcn_readlane(ids, P < BN ? (k_key0[u] >> log2P) : 0));
-      pgv[u] = fix(__builtin_amdgcn_readlane(ids, v_pi[u]));
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int b = wave * NU + u;
-      int pk_ = pgk[u];
-      if (k_split) pk_ = fix(__shfl(ids, swap_bits23(b * KROWS_U + lane / (D / 8)) >> log2P));  // lane's own page
-      const int ko = P > BN ? (j0 & (P - 1)) * D : 0;
-      load_lds16(kpg + (int64_t)pk_ * page_elems + k_loff[u] + ko, &sm.k[buf][b * 512]);
-      const int vo = P > BN ? (j0 & (P - 1)) : 0;
-      load_lds16(vpg + (int64_t)pgv[u] * page_elems + v_loff[u] + vo, &sm.v[buf][b * 512]);
-    }
-  };
-
-  f32x16 oacc[NB][ND];
-  float mrun[NB], lsum[NB];
-#pragma unroll
-  for (int n = 0; n < NB; ++n) {
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[n][db] = f32x16{};
-    mrun[n] = kNegBig;
-    lsum[n] = 0.f;
-  }
-  const float c2 = p.scale_log2;
-
-  // Loads retire in issue order.  Order per step: data of the next tile, then the page ids of the
-  // tile after it; at the end of the step the next tile's data must be in LDS and only the id load
-  // (when one was issued) may still be in flight.
-  constexpr int WAIT_ALL = 0x0f70;      // vmcnt(0)
-  constexpr int WAIT_BUT_ONE = 0x0f71;  // vmcnt(1)
-  int ids = load_ids(tr.tile(0));
-  issue_tile(tr.tile(0), 0, ids);
-  bool ids_pending = ntiles > 1;
-  if (ids_pending) ids = load_ids(tr.tile(1));
-  if (ids_pending) __builtin_amdgcn_s_waitcnt(WAIT_BUT_ONE);
-  else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
-  __syncthreads();
-
-  int buf = 0;
-  for (int idx = 0; idx < ntiles; ++idx) {
-    const bool more = idx + 1 < ntiles;
-    ids_pending = false;
-    if (more) {
-      issue_tile(tr.tile(idx + 1), buf ^ 1, ids);
-      ids_pending = idx + 2 < ntiles;
-      if (ids_pending) ids = load_ids(tr.tile(idx + 2));
-    }
-    const int j0 = tr.tile(idx) * BN;
-    const bool skip = wmax < 0 || j0 > wmax ||
-                      (cls == RK_LOCAL && j0 >= p.sink && j0 + BN - 1 <= wmin - p.window);
-    const bool full = j0 + BN - 1 <= wmin &&
-                      (cls == RK_GLOBAL || j0 + BN <= p.sink || j0 > wmax - p.window);
-    if (!skip) {
-      const bf16_t *Kb = sm.k[buf];
-      const bf16_t *Vb = sm.v[buf];
-      // S^T for the tile's 64 keys (two 32-key blocks) x this wave's NB x 32 queries
-      f32x16 s[NB][2];
-#pragma unroll
-      for (int n = 0; n < NB; ++n) s[n][0] = s[n][1] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + k_rd[c] + 32 * kb * D);
-#pragma unroll
-          for (int n = 0; n < NB; ++n) s[n][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[n][c], s[n][kb], 0, 0, 0);
-        }
-      bf16x8 pk[NB][2][2];
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        if (!full) {
-          // key of register i of block kb: jb + 16 * (i / 8) + i % 8, jb = j0 + 32 kb + 8 hl
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const int jb = j0 + 32 * kb + 8 * hl;
-            const int hi = pos[n] - jb;     // visible: off <= hi
-            const int lo = win_lo[n] - jb;  // local: off >= lo, or off < sk
-            const int sk = p.sink - jb;
-            if (cls == RK_GLOBAL) {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int off = 16 * (i >> 3) + (i & 7);
-                s[n][kb][i] = off <= hi ? s[n][kb][i] : -INFINITY;
-              }
-            } else {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int off = 16 * (i >> 3) + (i & 7);
-                s[n][kb][i] = (off <= hi && (off >= lo || off < sk)) ? s[n][kb][i] : -INFINITY;
-              }
-            }
-          }
-        }
-        float mt = s[n][0][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[n][0][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[n][1][i]);
-        mt = halves_max(mt);
-        const float mts = mt * c2;
-        if (__any(mts > mrun[n] + kRescaleSlack)) {
-          const float mnew = fmaxf(mrun[n], mts);
-          const float alpha = fast_exp2(mrun[n] - mnew);
-#pragma unroll
-          for (int db = 0; db < ND; ++db) oacc[n][db] *= alpha;
-          lsum[n] *= alpha;
-          mrun[n] = mnew;
-        }
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          f32x8 e0, e1;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            e0[i] = fast_exp2(fmaf(s[n][kb][i], c2, -mrun[n]));
-            e1[i] = fast_exp2(fmaf(s[n][kb][i + 8], c2, -mrun[n]));
-            ps += e0[i] + e1[i];
-          }
-          pk[n][kb][0] = __builtin_convertvector(e0, bf16x8);
-          pk[n][kb][1] = __builtin_convertvector(e1, bf16x8);
-        }
-        lsum[n] += ps;
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Vb + v_rd[2 * kb + cc] + 32 * db * Pt);
-#pragma unroll
-            for (int n = 0; n < NB; ++n)
-              oacc[n][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[n][kb][cc], oacc[n][db], 0, 0, 0);
-          }
-    }
-    if (ids_pending) __builtin_amdgcn_s_waitcnt(WAIT_BUT_ONE);
-    else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
-    __syncthreads();
-    buf ^= 1;
-  }
-
-  // ---- epilogue: O^T accumulator (lane column = query, 16 channels per 32-channel block)
-#pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    const float lt = halves_sum(lsum[n]);
-    if (!valid[n]) continue;
-    const float inv = 1.0f / lt;
-    bf16_t *orow = static_cast<bf16_t *>(p.o) + ((int64_t)(si.cu_q + tq[n]) * p.H + hq[n]) * D;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        f32x4 w = {oacc[n][db][4 * a4 + 0] * inv, oacc[n][db][4 * a4 + 1] * inv, oacc[n][db][4 * a4 + 2] * inv,
-                   oacc[n][db][4 * a4 + 3] * inv};
-        *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * a4 + 4 * hl) = __builtin_convertvector(w, bf16x4);
-      }
-    if (p.lse && hl == 0)
-      p.lse[(int64_t)hq[n] * p.total_q + si.cu_q + tq[n]] = (mrun[n] + log2f(lt)) * 0.69314718055994531f;
-  }
-}
-
-// ------------------------------------------------------------------------------------------------
-// bf16 attention, ping-pong: two groups of four waves (one wave of each group per SIMD) run the same
-// per-half-tile work shifted by half a tile, so that while one wave of a SIMD runs its softmax on
-// the vector ALUs the other keeps the matrix cores busy.  With both groups in step (one barrier per
-// tile), the two waves of a SIMD would run their MFMA phases together and then their softmax phases
-// together.
-//   group A, tile t:  QK(h0) | softmax(h0) | QK(h1) + PV(h0) | softmax(h1) | PV(h1)
-//   group B, tile t:  softmax(t-1, h1) | PV(t-1, h1) + QK(h0) | softmax(h0) | QK(h1) + PV(h0)
-// (h0, h1 = keys 0-31 and 32-63 of the tile).  Group B finishes a tile's second half in the next
-// iteration, so tiles stay in LDS for one iteration longer: four stages.
-// ------------------------------------------------------------------------------------------------
-
-template <int D>
-struct AttnPPSmem {
-  static constexpr int NSTAGE = 4;
-  bf16_t k[NSTAGE][BN * D];
-  bf16_t v[NSTAGE][D * BN];
-};
-
-#ifndef RK_PP_GROUP_SHIFT
-#define RK_PP_GROUP_SHIFT 2  // group = wave >> 2: waves w and w + 4 share a SIMD
-#endif
-
-template <int D>
-__global__ void __launch_bounds__(512, 1) attn_bf16_pp(AttnParams p) {
-  constexpr int NWAVES = 8;
-  constexpr int NC = D / 16;
-  constexpr int ND = D / 32;
-  constexpr int UNITS = BN * D * 2 / 1024;
-  constexpr int NU = UNITS / NWAVES;
-  constexpr int KROWS_U = 512 / D;
-  static_assert(NU >= 1 && UNITS % NWAVES == 0, "tile does not split over the waves");
-  __shared__ __attribute__((aligned(1024))) AttnPPSmem<D> sm;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int group = RK_PP_GROUP_SHIFT == 2 ? (wave >> 2) : (wave & 1);
-  const int lane = tid & 63, hl = lane >> 5, m = lane & 31;
-  const Item it = p.items[blockIdx.x];
-  if (it.seq < 0) return;  // schedule padding: keeps the next items on their XCD
-  const SeqInfo si = p.seqs[it.seq];
-  const int g = it.kv_head;
-  const int cls = p.head_class[g];
-  const int tok_end = min(it.tok0 + p.T, si.n_q);
-  const int L = si.kv_len;
-  const int i_max = si.q_start + tok_end - 1;
-  const TileRange tr = tile_range(cls, si.q_start + it.tok0, i_max, p.sink, p.window);
-  const int ntiles = tr.count();
-  const int32_t *__restrict__ pt = p.page_ids + p.page_base[g * p.num_seqs + it.seq];
-  const bf16_t *__restrict__ kpg = static_cast<const bf16_t *>(p.k_pages);
-  const bf16_t *__restrict__ vpg = static_cast<const bf16_t *>(p.v_pages);
-  const int P = p.P, log2P = p.log2P;
-  const int Pt = P < BN ? P : BN;
-  const int n_logical = (L + P - 1) >> log2P;
-  const int64_t page_elems = (int64_t)P * D;
-  const int pg_fallback = pt[i_max >> log2P];
-
   // ---- the query row (column of S^T) this lane owns
   const int r = wave * 32 + m;
   const int hh = r / p.T;
@@ -481,7 +195,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp(AttnParams p) {
   const bool valid = hh < p.G && tq < tok_end;
   const int pos = valid ? si.q_start + tq : -1;
   const int hq = g * p.G + hh;
-  const int win_lo = cls == RK_GLOBAL ? 0 : pos - p.window + 1;
+  const int win_lo = cls == RK_GLOBAL ? 0 : pos - p.window + 1;  // first window key of the row
+  // wave-uniform query range: scalar registers, so tile classes are scalar branches
   const int wmin = __builtin_amdgcn_readfirstlane(wave_min(valid ? pos : INT32_MAX));
   const int wmax = __builtin_amdgcn_readfirstlane(wave_max(pos));
 
@@ -495,58 +210,93 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp(AttnParams p) {
     }
   }
 
-  // ---- tile-invariant geometry of this wave's 1 KB load blocks (same image as attn_bf16)
-  int k_key0[NU], k_loff[NU], v_pi[NU], v_loff[NU];
-  const bool k_split = D == 64 && P < 16;
+  // ---- tile-invariant geometry of this wave's 1 KB load blocks (block b = wave * NU + u)
+  int k_key0[NU], v_pi[NU];         // K: first key of the block (uniform); V: page-in-tile
+  uint32_t k_loff[NU], v_loff[NU];  // lane's byte offset in its page (unsigned 32-bit: the load
+                                    // takes a scalar page address plus a lane offset)
+  // a D = 64 K block spans 8 keys; with 8-key pages its two 4-key halves come from two pages
+  constexpr bool k_split = D == 64 && SMALLP;
+  constexpr bool v_split = SMALLP;
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     const int b = wave * NU + u;
+    // K: LDS rows b*KROWS_U + lane/(D/8), slot lane % (D/8)
     const int row = b * KROWS_U + lane / (D / 8);
     const int slot = lane % (D / 8);
     const int key = swap_bits23(row);
     const int chunk = slot ^ kswz<D>(row);
     k_key0[u] = swap_bits23(b * KROWS_U) & ~(KROWS_U - 1);
-    k_loff[u] = (P <= BN ? (key & (P - 1)) : key) * D + chunk * 8;
-    const int upp = D * Pt * 2 / 1024;
-    const int rows_u = 512 / Pt;
-    const int d = (b % upp) * rows_u + lane / (Pt / 8);
-    const int cg = (lane % (Pt / 8)) ^ vswz(d, Pt);
-    v_pi[u] = b / upp;
-    v_loff[u] = d * P + cg * 8;
+    // pages of up to 64 keys: the tile starts on a page boundary; larger pages: + tile offset per tile
+    k_loff[u] = ((P <= BN ? (key & (P - 1)) : key) * D + chunk * 8) * 2;
+    // V: block b of the [D / 32][page-in-tile][32][Pt] image; the lane fills elements e .. e + 7
+    const int e = 512 * b + 8 * lane;
+    const int r2 = e % (32 * BN), r3 = r2 % (32 * Pt);
+    const int d = 32 * (e / (32 * BN)) + r3 / Pt;
+    const int cg = ((r3 % Pt) >> 3) ^ vswz(d, Pt);
+    // page-in-tile: uniform over the block, except with 8-key pages (lanes 32-63 take the next page)
+    v_pi[u] = v_split ? r2 / (32 * Pt) : ((512 * b) % (32 * BN)) / (32 * Pt);
+    v_loff[u] = (d * P + cg * 8) * 2;   // + (j0 & (P - 1)) keys when P > 64
   }
+  // V^T read offsets (elements) for the four (kb, cc) key chunks of a 64-key tile, channel row m of
+  // the first 32-channel block; block db is 32 * BN elements further (vswz(m + 32 db) = vswz(m))
   int v_rd[4];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
-    const int k8 = 2 * q4 + hl;
+    const int k8 = 2 * q4 + hl;  // 8-key chunk 4kb + 2cc + hl
     const int cpr = Pt / 8;
-    v_rd[q4] = (k8 / cpr) * D * Pt + m * Pt + (((k8 % cpr) ^ vswz(m, Pt)) << 3);
+    v_rd[q4] = (k8 / cpr) * 32 * Pt + m * Pt + (((k8 % cpr) ^ vswz(m, Pt)) << 3);
   }
+  // K read offsets (elements) for the NC channel chunks, rows m (+32 for the second key block)
   int k_rd[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) k_rd[c] = m * D + (((2 * c + hl) ^ kswz<D>(m)) << 3);
 
-  auto page_of = [&](int lp) -> int {
-    const int pg = lp < n_logical ? pt[lp] : -1;
-    return pg >= 0 ? pg : pg_fallback;
-  };
-  auto issue_tile = [&](int tile, int buf) {
-    const int j0 = tile * BN;
-    int pgk[NU], pgv[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      pgk[u] = page_of((j0 + k_key0[u]) >> log2P);
-      pgv[u] = page_of((j0 >> log2P) + v_pi[u]);
+  // Page ids of a step's tiles: one vector load per wave (lane x * npt + i holds the id of page i
+  // of the step's x-th tile), issued a step ahead and read back with readlane, so the lookup latency
+  // stays off the critical path and no scalar load shares the LDS wait counter with operand reads.
+  const int npt = P < BN ? BN / P : 1;
+  auto load_ids = [&](int step) -> int {
+    const int x = lane / npt, i = lane - x * npt;
+    const int t = step * TPS + x;
+    int v = -1;
+    if (x < TPS && t < ntiles) {
+      const int lp = ((tr.tile(t) * BN) >> log2P) + i;
+      if (lp < n_logical) v = pt[lp];
     }
+    return v;
+  };
+  auto fix = [&](int pg) { return pg >= 0 ? pg : pg_fallback; };
+  // loads of the step's x-th tile (key tile `tile`) into slot x of buffer buf
+  auto issue_tile = [&](int tile, int buf, int x, int ids) {
+    const int j0 = tile * BN;
+    const int lane0 = x * npt;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int b = wave * NU + u;
-      int pk_ = pgk[u];
-      if (k_split) pk_ = page_of((j0 + swap_bits23(b * KROWS_U + lane / (D / 8))) >> log2P);
       const int ko = P > BN ? (j0 & (P - 1)) * D : 0;
-      load_lds16(kpg + (int64_t)pk_ * page_elems + k_loff[u] + ko, &sm.k[buf][b * 512]);
+      if constexpr (k_split) {
+        const int pg = fix(__shfl(ids, lane0 + (swap_bits23(b * KROWS_U + lane / (D / 8)) >> log2P)));
+        load_lds16(reinterpret_cast<const char *>(kpg + (int64_t)pg * page_elems + ko) + k_loff[u], &sm.k[buf][x][b * 512]);
+      } else {
+        const int pg = fix(__builtin_amdgcn_readlane(ids, lane0 + (P < BN ? (k_key0[u] >> log2P) : 0)));
+        const char *page = reinterpret_cast<const char *>(kpg + (int64_t)pg * page_elems + ko);  // uniform
+        load_lds16(page + opaque(k_loff[u]), &sm.k[buf][x][b * 512]);
+      }
       const int vo = P > BN ? (j0 & (P - 1)) : 0;
-      load_lds16(vpg + (int64_t)pgv[u] * page_elems + v_loff[u] + vo, &sm.v[buf][b * 512]);
+      if constexpr (v_split) {
+        const int pg = fix(__shfl(ids, lane0 + v_pi[u]));
+        load_lds16(reinterpret_cast<const char *>(vpg + (int64_t)pg * page_elems + vo) + v_loff[u], &sm.v[buf][x][b * 512]);
+      } else {
+        const int pg = fix(__builtin_amdgcn_readlane(ids, lane0 + v_pi[u]));
+        const char *page = reinterpret_cast<const char *>(vpg + (int64_t)pg * page_elems + vo);  // uniform
+        load_lds16(page + opaque(v_loff[u]), &sm.v[buf][x][b * 512]);
+      }
     }
+  };
+  auto issue_step = [&](int step, int buf, int ids) {
+#pragma unroll
+    for (int x = 0; x < TPS; ++x)
+      if (step * TPS + x < ntiles) issue_tile(tr.tile(step * TPS + x), buf, x, ids);
   };
 
   f32x16 oacc[ND];
@@ -555,46 +305,53 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp(AttnParams p) {
   float mrun = kNegBig, lsum = 0.f;
   const float c2 = p.scale_log2;
 
-  // per-tile classes for this wave
-  auto tile_skip = [&](int j0) {
-    return wmax < 0 || j0 > wmax || (cls == RK_LOCAL && j0 >= p.sink && j0 + BN - 1 <= wmin - p.window);
-  };
-  auto tile_full = [&](int j0) {
-    return j0 + BN - 1 <= wmin && (cls == RK_GLOBAL || j0 + BN <= p.sink || j0 > wmax - p.window);
-  };
-  // S^T of one 32-key half (kb) of the tile in stage `buf`
-  auto qk_half = [&](int buf, int kb, f32x16 &s) {
-    const bf16_t *Kb = sm.k[buf] + 32 * kb * D;
-    s = f32x16{};
+  // one 64-key tile: first key j0, operands in Kb / Vb
+  auto tile_compute = [&](const int j0, const bf16_t *Kb, const bf16_t *Vb) __attribute__((always_inline)) {
+    const bool skip = wmax < 0 || j0 > wmax ||
+                      (cls == RK_LOCAL && j0 >= p.sink && j0 + BN - 1 <= wmin - p.window);
+    const bool full = j0 + BN - 1 <= wmin &&
+                      (cls == RK_GLOBAL || j0 + BN <= p.sink || j0 > wmax - p.window);
+    if (skip) return;
+    // S^T for the tile's 64 keys (two 32-key blocks) x this wave's 32 queries
+    f32x16 s[2] = {};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + k_rd[c]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s, 0, 0, 0);
-    }
-  };
-  // mask, online-softmax update and bf16 pack of one half; pk[cc] = keys 16 cc .. 16 cc + 15 of the half
-  auto soft_half = [&](int j0, bool full, int kb, f32x16 &s, bf16x8 (&pk)[2]) {
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + k_rd[c] + 32 * kb * D);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+      }
     if (!full) {
-      const int jb = j0 + 32 * kb + 8 * hl;
-      const int hi = pos - jb, lo = win_lo - jb, sk = p.sink - jb;
-      if (cls == RK_GLOBAL) {
+      // key of register i of block kb: jb + 16 * (i / 8) + i % 8, jb = j0 + 32 kb + 8 hl
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int off = 16 * (i >> 3) + (i & 7);
-          s[i] = off <= hi ? s[i] : -INFINITY;
-        }
-      } else {
+      for (int kb = 0; kb < 2; ++kb) {
+        const int jb = j0 + 32 * kb + 8 * hl;
+        const int hi = pos - jb;     // visible: off <= hi
+        const int lo = win_lo - jb;  // local: off >= lo, or off < sk
+        const int sk = p.sink - jb;
+        if (cls == RK_GLOBAL) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int off = 16 * (i >> 3) + (i & 7);
-          s[i] = (off <= hi && (off >= lo || off < sk)) ? s[i] : -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int off = 16 * (i >> 3) + (i & 7);
+            s[kb][i] = off <= hi ? s[kb][i] : -INFINITY;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int off = 16 * (i >> 3) + (i & 7);
+            s[kb][i] = (off <= hi && (off >= lo || off < sk)) ? s[kb][i] : -INFINITY;
+          }
         }
       }
     }
-    float mt = s[0];
+    float mt = s[0][0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
     mt = halves_max(mt);
+    // The running max is only raised when a score exceeds it by more than 2^8 in the exp2 domain;
+    // O and the row sum are rescaled then.
     const float mts = mt * c2;
     if (__any(mts > mrun + kRescaleSlack)) {
       const float mnew = fmaxf(mrun, mts);
@@ -604,94 +361,70 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp(AttnParams p) {
       lsum *= alpha;
       mrun = mnew;
     }
-    f32x8 e0, e1;
+    // bf16 weights; pk[kb][cc] is the B operand of the PV product for keys 32 kb + 16 cc .. + 15
+    bf16x8 pk[2][2];
     float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      e0[i] = fast_exp2(fmaf(s[i], c2, -mrun));
-      e1[i] = fast_exp2(fmaf(s[i + 8], c2, -mrun));
-      ps += e0[i] + e1[i];
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x8 e0, e1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e0[i] = fast_exp2(fmaf(s[kb][i], c2, -mrun));
+        e1[i] = fast_exp2(fmaf(s[kb][i + 8], c2, -mrun));
+        ps += e0[i] + e1[i];
+      }
+      pk[kb][0] = __builtin_convertvector(e0, bf16x8);
+      pk[kb][1] = __builtin_convertvector(e1, bf16x8);
     }
     lsum += ps;
-    pk[0] = __builtin_convertvector(e0, bf16x8);
-    pk[1] = __builtin_convertvector(e1, bf16x8);
-  };
-  auto pv_half = [&](int buf, int kb, const bf16x8 (&pk)[2]) {
-    const bf16_t *Vb = sm.v[buf];
+    // O^T += V^T P^T
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Vb + v_rd[2 * kb + cc] + 32 * db * Pt);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[cc], oacc[db], 0, 0, 0);
-      }
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Vb + v_rd[2 * kb + cc] + db * 32 * BN);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kb][cc], oacc[db], 0, 0, 0);
+        }
   };
 
-  issue_tile(tr.tile(0), 0);
-  if (ntiles > 1) issue_tile(tr.tile(1), 1);
-  __builtin_amdgcn_s_waitcnt(0x0f70);
+  // Loads retire in issue order.  Order per step: data of the next step, then the page ids of the
+  // step after it; at the end of the step the next step's data must be in LDS and only the id load
+  // (when one was issued) may still be in flight.
+  constexpr int WAIT_ALL = 0x0f70;      // vmcnt(0)
+  constexpr int WAIT_BUT_ONE = 0x0f71;  // vmcnt(1)
+  int ids = load_ids(0);
+  issue_step(0, 0, ids);
+  bool ids_pending = nsteps > 1;
+  if (ids_pending) ids = load_ids(1);
+  if (ids_pending) __builtin_amdgcn_s_waitcnt(WAIT_BUT_ONE);
+  else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
   __syncthreads();
 
-  // The two groups run separate loops (same number of barriers) so that each loop's registers are
-  // allocated on their own.
-  if (group == 0) {
-    for (int idx = 0; idx < ntiles; ++idx) {
-      const int buf = idx & 3;
-      if (idx + 2 < ntiles) issue_tile(tr.tile(idx + 2), (idx + 2) & 3);
-      const int j0 = tr.tile(idx) * BN;
-      if (!tile_skip(j0)) {
-        const bool full = tile_full(j0);
-        f32x16 s0, s1;
-        bf16x8 pk0[2], pk1[2];
-        // phase boundaries are scheduling barriers: the order of MFMA and softmax phases is the point
-        qk_half(buf, 0, s0);
-        __builtin_amdgcn_sched_barrier(0);
-        soft_half(j0, full, 0, s0, pk0);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_half(buf, 1, s1);
-        pv_half(buf, 0, pk0);
-        __builtin_amdgcn_sched_barrier(0);
-        soft_half(j0, full, 1, s1, pk1);
-        __builtin_amdgcn_sched_barrier(0);
-        pv_half(buf, 1, pk1);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0f70);
-      __syncthreads();
+  // One step.  The LDS buffer index is a template constant (the loop below is unrolled by two),
+  // so every operand address is a lane register plus an immediate offset.
+  auto step = [&](const int s, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    ids_pending = false;
+    if (s + 1 < nsteps) {
+      issue_step(s + 1, buf ^ 1, ids);
+      ids_pending = s + 2 < nsteps;
+      if (ids_pending) ids = load_ids(s + 2);
     }
-  } else {
-    f32x16 s0, s1;  // s1: second half of the previous tile, finished in the next iteration
-    int j0_prev = 0;
-    bool skip_prev = true, full_prev = true;
-    for (int idx = 0; idx < ntiles; ++idx) {
-      const int buf = idx & 3;
-      if (idx + 2 < ntiles) issue_tile(tr.tile(idx + 2), (idx + 2) & 3);
-      const int j0 = tr.tile(idx) * BN;
-      const bool skip = tile_skip(j0), full = tile_full(j0);
-      bf16x8 pk0[2], pk1[2];
-      if (!skip_prev) soft_half(j0_prev, full_prev, 1, s1, pk1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (!skip) qk_half(buf, 0, s0);
-      if (!skip_prev) pv_half((idx - 1) & 3, 1, pk1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (!skip) {
-        soft_half(j0, full, 0, s0, pk0);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_half(buf, 1, s1);
-        pv_half(buf, 0, pk0);
-      }
-      j0_prev = j0;
-      skip_prev = skip;
-      full_prev = full;
-      __builtin_amdgcn_s_waitcnt(0x0f70);
-      __syncthreads();
-    }
-    if (!skip_prev) {
-      bf16x8 pk1[2];
-      soft_half(j0_prev, full_prev, 1, s1, pk1);
-      pv_half((ntiles - 1) & 3, 1, pk1);
-    }
+#pragma unroll
+    for (int x = 0; x < TPS; ++x)
+      if (s * TPS + x < ntiles) tile_compute(tr.tile(s * TPS + x) * BN, sm.k[buf][x], sm.v[buf][x]);
+    if (ids_pending) __builtin_amdgcn_s_waitcnt(WAIT_BUT_ONE);
+    else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    __syncthreads();
+  };
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, IntC<0>{});
+    if (s + 1 < nsteps) step(s + 1, IntC<1>{});
   }
 
+  // ---- epilogue: O^T accumulator (lane column = query, 16 channels per 32-channel block)
   const float lt = halves_sum(lsum);
   if (!valid) return;
   const float inv = 1.0f / lt;
@@ -948,18 +681,14 @@ hipError_t launch_attention(const AttnParams &p, int dtype, int head_dim, hipStr
   if (p.n_items <= 0) return hipSuccess;
   dim3 grid(p.n_items);
   if (dtype == RK_BF16) {
-#ifdef RK_ATTN_PINGPONG
-    if (head_dim == 128)
-      hipLaunchKernelGGL(attn_bf16_pp<128>, grid, dim3(512), 0, stream, p);
-    else
-      hipLaunchKernelGGL(attn_bf16_pp<64>, grid, dim3(512), 0, stream, p);
-#else
-    constexpr int NT = kRowsPerItem / RK_ATTN_NB * 2;
-    if (head_dim == 128)
-      hipLaunchKernelGGL((attn_bf16<128, RK_ATTN_NB>), grid, dim3(NT), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_bf16<64, RK_ATTN_NB>), grid, dim3(NT), 0, stream, p);
-#endif
+    const dim3 block(2 * kRowsPerItem);
+    if (head_dim == 128) {
+      if (p.P < 16) hipLaunchKernelGGL((attn_bf16<128, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((attn_bf16<128, false>), grid, block, 0, stream, p);
+    } else {
+      if (p.P < 16) hipLaunchKernelGGL((attn_bf16<64, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((attn_bf16<64, false>), grid, block, 0, stream, p);
+    }
   } else {
     if (head_dim == 128)
       hipLaunchKernelGGL(attn_f32<128>, grid, dim3(kF32Threads), 0, stream, p);
