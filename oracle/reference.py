@@ -8,6 +8,12 @@ over the full context and local heads over their paged sink + window KV ([AB]
 使い方, EXECUTE item).  Here the cache is a dense [Hkv][L][D] array per
 sequence, and attention is the dense masked definition of `attention`.
 
+Head-ragged query ranges (EXECUTE's split, same item): a workload may give the
+GLOBAL heads an earlier first query position than the LOCAL heads.  GLOBAL heads
+then recompute those positions and write their new KV from there; LOCAL heads
+keep the reused KV below their own start and query only from it.  A sequence's
+packed rows begin at the earlier start.
+
 The cache stores keys in the storage dtype, so a re-rotated key is rounded once
 to that dtype before attention reads it (`round_store`).
 
@@ -21,6 +27,8 @@ import numpy as np
 import torch
 
 from . import attention, rope
+
+LOCAL, GLOBAL = 0, 1
 
 
 def to64(t: torch.Tensor) -> np.ndarray:
@@ -38,45 +46,87 @@ def rerotated_keys(doc, head_dim: int, base: float, style: int, dtype: Optional[
     return round_store(k, dtype) if dtype is not None else k
 
 
-def sequence_kv(inp, seq: int, rope_style: int = rope.ROTATE_HALF):
-    """Dense fp64 K, V [Hkv][kv_len][D] of one sequence after reuse import and append."""
+def _new_rows(inp, seq: int, kv_head: int):
+    """(first position, fp64 K rows, fp64 V rows) that the call writes for one (sequence, KV head):
+    from the head's class start to kv_len.  The packed rows of a sequence begin at q_begin."""
     wl = inp.wl
-    L, qs = wl.kv_lens[seq], wl.q_starts[seq]
-    Hkv, D = wl.num_kv_heads, wl.head_dim
-    k = np.full((Hkv, L, D), np.nan)
-    v = np.full((Hkv, L, D), np.nan)
+    cls = int(wl.head_class[wl.layer, kv_head])
+    a, L = wl.q_start_of(seq, cls), wl.kv_lens[seq]
+    cu = wl.cu_q()
+    r0 = cu[seq] + (a - wl.q_begin(seq))
+    return a, to64(inp.k_new[r0:cu[seq + 1], kv_head]), to64(inp.v_new[r0:cu[seq + 1], kv_head])
+
+
+def head_kv(inp, seq: int, kv_head: int, rope_style: int = rope.ROTATE_HALF):
+    """Dense fp64 K, V [kv_len][D] of one (sequence, KV head) after reuse import and append.
+
+    Reused documents fill their token ranges with re-rotated keys; then the call's new keys and values
+    overwrite the positions from the head's class start on.  Under EXECUTE's split ([AB] 使い方,
+    EXECUTE item) a GLOBAL head recomputes from its own, earlier start and so writes the online KV
+    there too, while a LOCAL head keeps the reused KV below its start."""
+    wl = inp.wl
+    L, D = wl.kv_lens[seq], wl.head_dim
+    k = np.full((L, D), np.nan)
+    v = np.full((L, D), np.nan)
     for doc in inp.docs:
         if doc.seq != seq:
             continue
         sl = slice(doc.tok_begin, doc.tok_begin + doc.n_tok)
-        k[:, sl] = rerotated_keys(doc, D, wl.rope_base, rope_style, wl.dtype)
-        v[:, sl] = to64(doc.v_off)
-    cu = wl.cu_q()
-    k[:, qs:L] = to64(inp.k_new[cu[seq]:cu[seq + 1]]).transpose(1, 0, 2)
-    v[:, qs:L] = to64(inp.v_new[cu[seq]:cu[seq + 1]]).transpose(1, 0, 2)
+        kk = rope.rotate(to64(doc.k_off[kv_head]), doc.delta, wl.rope_base, rope_style)
+        k[sl] = round_store(kk, wl.dtype)
+        v[sl] = to64(doc.v_off[kv_head])
+    a, kn, vn = _new_rows(inp, seq, kv_head)
+    k[a:L] = kn
+    v[a:L] = vn
     if np.isnan(k).any() or np.isnan(v).any():
         raise ValueError("sequence %d has prefix tokens that no reused document covers" % seq)
     return k, v
 
 
+def sequence_kv(inp, seq: int, rope_style: int = rope.ROTATE_HALF):
+    """Dense fp64 K, V [Hkv][kv_len][D] of one sequence: `head_kv` for every KV head."""
+    wl = inp.wl
+    kv = [head_kv(inp, seq, g, rope_style) for g in range(wl.num_kv_heads)]
+    return np.stack([x[0] for x in kv]), np.stack([x[1] for x in kv])
+
+
 def prefill_seq(inp, seq: int, rows: Optional[Sequence[int]] = None, scale: Optional[float] = None,
                 rope_style: int = rope.ROTATE_HALF):
-    """o [H][n][D], lse [H][n] (fp64) for the given query rows (0-based within the sequence's queries)."""
+    """o [H][n][D], lse [H][n] (fp64) for the given rows of the sequence's packed queries (row r is
+    position q_begin + r).  A head computes the rows from its class start on; a LOCAL head's rows
+    below its start (EXECUTE's split) are not part of the call and come back as NaN."""
     wl = inp.wl
     cu = wl.cu_q()
     k, v = sequence_kv(inp, seq, rope_style)
     q = to64(inp.q[cu[seq]:cu[seq + 1]]).transpose(1, 0, 2)
+    n = q.shape[1]
+    rows = np.arange(n) if rows is None else np.asarray(rows, np.int64)
     kv_class = wl.head_class[wl.layer]
-    return attention.attention_heads(q, k, v, kv_class, wl.q_starts[seq], wl.sink, wl.window, scale,
-                                     None if rows is None else np.asarray(rows))
+    qb = wl.q_begin(seq)
+    if scale is None:
+        scale = 1.0 / np.sqrt(wl.head_dim)
+    o = np.full((wl.num_q_heads, len(rows), wl.head_dim), np.nan)
+    lse = np.full((wl.num_q_heads, len(rows)), np.nan)
+    masks = {}
+    for h in range(wl.num_q_heads):
+        g = h // wl.group
+        cls = int(kv_class[g])
+        if cls not in masks:
+            sel = np.nonzero(rows >= wl.q_start_of(seq, cls) - qb)[0]
+            masks[cls] = (sel, attention.visibility_mask(cls, qb + rows[sel], wl.kv_lens[seq], wl.sink, wl.window))
+        sel, mask = masks[cls]
+        if len(sel):
+            o[h, sel], lse[h, sel] = attention.masked_attention(q[h, rows[sel]], k[g], v[g], mask, scale)
+    return o, lse
 
 
 def prefill(inp, scale: Optional[float] = None, rope_style: int = rope.ROTATE_HALF):
-    """The whole call: o [total_q][H][D] and lse [H][total_q], fp64."""
+    """The whole call: o [total_q][H][D] and lse [H][total_q], fp64 (NaN where a LOCAL head's rows
+    precede its start)."""
     wl = inp.wl
     H, D = wl.num_q_heads, wl.head_dim
-    o = np.empty((wl.total_q, H, D))
-    lse = np.empty((H, wl.total_q))
+    o = np.full((wl.total_q, H, D), np.nan)
+    lse = np.full((H, wl.total_q), np.nan)
     cu = wl.cu_q()
     for b in range(wl.num_seqs):
         if cu[b + 1] == cu[b]:
@@ -87,39 +137,20 @@ def prefill(inp, scale: Optional[float] = None, rope_style: int = rope.ROTATE_HA
     return o, lse
 
 
-def head_kv(inp, seq: int, kv_head: int, rope_style: int = rope.ROTATE_HALF):
-    """Dense fp64 K, V [kv_len][D] of one (sequence, KV head): the slice of `sequence_kv` for that head."""
-    wl = inp.wl
-    L, qs = wl.kv_lens[seq], wl.q_starts[seq]
-    D = wl.head_dim
-    k = np.full((L, D), np.nan)
-    v = np.full((L, D), np.nan)
-    for doc in inp.docs:
-        if doc.seq != seq:
-            continue
-        sl = slice(doc.tok_begin, doc.tok_begin + doc.n_tok)
-        kk = rope.rotate(to64(doc.k_off[kv_head]), doc.delta, wl.rope_base, rope_style)
-        k[sl] = round_store(kk, wl.dtype)
-        v[sl] = to64(doc.v_off[kv_head])
-    cu = wl.cu_q()
-    k[qs:L] = to64(inp.k_new[cu[seq]:cu[seq + 1], kv_head])
-    v[qs:L] = to64(inp.v_new[cu[seq]:cu[seq + 1], kv_head])
-    if np.isnan(k).any() or np.isnan(v).any():
-        raise ValueError("sequence %d has prefix tokens that no reused document covers" % seq)
-    return k, v
-
-
 def prefill_rows(inp, seq: int, q_head: int, rows, scale: Optional[float] = None,
                  rope_style: int = rope.ROTATE_HALF):
-    """o [n][D], lse [n] (fp64) of one q head for the given query rows of one sequence."""
+    """o [n][D], lse [n] (fp64) of one q head for the given packed rows of one sequence (rows at or
+    after the head's class start)."""
     wl = inp.wl
     g = q_head // wl.group
     k, v = head_kv(inp, seq, g, rope_style)
     rows = np.asarray(rows, np.int64)
+    cls = int(wl.head_class[wl.layer, g])
+    if len(rows) and rows.min() < wl.q_start_of(seq, cls) - wl.q_begin(seq):
+        raise ValueError("row before the head's class start")
     cu = wl.cu_q()
     q = to64(inp.q[cu[seq] + torch.from_numpy(rows).to(inp.q.device), q_head])
     if scale is None:
         scale = 1.0 / np.sqrt(wl.head_dim)
-    cls = int(wl.head_class[wl.layer, g])
-    mask = attention.visibility_mask(cls, wl.q_starts[seq] + rows, wl.kv_lens[seq], wl.sink, wl.window)
+    mask = attention.visibility_mask(cls, wl.q_begin(seq) + rows, wl.kv_lens[seq], wl.sink, wl.window)
     return attention.masked_attention(q, k, v, mask, scale)

@@ -53,6 +53,9 @@ class Workload:
     rope_base: float = 1.0e6
     num_pages: int = 0            # pool size; 0 -> exactly what the call holds
     pool_slack: int = 0           # extra pages on top of what the call holds
+    # per sequence, first query position of the GLOBAL heads (None: q_starts).  GLOBAL heads then
+    # recompute queries from here while LOCAL heads query from q_starts (<= those, per sequence).
+    q_starts_global: Optional[List[int]] = None
 
     @property
     def group(self) -> int:
@@ -62,9 +65,17 @@ class Workload:
     def num_seqs(self) -> int:
         return len(self.kv_lens)
 
+    def q_begin(self, seq: int) -> int:
+        """First query position of the sequence's packed rows (the earlier of the two class starts)."""
+        return self.q_starts[seq] if self.q_starts_global is None else self.q_starts_global[seq]
+
+    def q_start_of(self, seq: int, cls: int) -> int:
+        """First query position of a head of class cls."""
+        return self.q_begin(seq) if cls == GLOBAL else self.q_starts[seq]
+
     @property
     def q_lens(self) -> List[int]:
-        return [L - s for L, s in zip(self.kv_lens, self.q_starts)]
+        return [L - self.q_begin(b) for b, L in enumerate(self.kv_lens)]
 
     @property
     def total_q(self) -> int:
@@ -144,8 +155,25 @@ def dsv4flash(layer: int = 3) -> Workload:
                     dtype=torch.bfloat16, head_class=_class_map_dsv4(10 * 5 + SEED_CLASS), doc_len=8192)
 
 
+def execute_split(wl: Workload, q_starts_global: Optional[Sequence[int]] = None, name: Optional[str] = None) -> Workload:
+    """The same call with EXECUTE's head-ragged query ranges: GLOBAL heads recompute from
+    q_starts_global (default 0: the whole prefix), LOCAL heads query from q_starts."""
+    qg = [0] * wl.num_seqs if q_starts_global is None else [int(x) for x in q_starts_global]
+    if any(g < 0 or g > s for g, s in zip(qg, wl.q_starts)):
+        raise ValueError("need 0 <= q_start_global <= q_start")
+    return dataclasses.replace(wl, q_starts_global=qg, name=name or wl.name + ", global heads recompute")
+
+
+def dsv4flash_split(layer: int = 3) -> Workload:
+    """DeepSeek-V4-Flash-style mixed layer under EXECUTE: the 8 GLOBAL heads recompute all 128K positions,
+    the 56 LOCAL heads query the last 8K over their reused sink + window KV."""
+    return execute_split(dsv4flash(layer), [0],
+                         name="DeepSeek-V4-Flash-style layer %d, EXECUTE split: global heads 128K queries, "
+                              "local heads 8K, 64 heads MHA" % layer)
+
+
 CONFIGS = {"tiny": tiny, "mistral7b": mistral7b, "llama70b": llama70b, "qwen32b": qwen32b,
-           "dsv4flash": dsv4flash}
+           "dsv4flash": dsv4flash, "dsv4flash_split": dsv4flash_split}
 
 
 def random_small(seed: int, dtype: torch.dtype = torch.bfloat16, allow_reuse: bool = True) -> Workload:
@@ -171,6 +199,21 @@ def random_small(seed: int, dtype: torch.dtype = torch.bfloat16, allow_reuse: bo
                     kv_lens=kv_lens, q_starts=q_starts, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
                     page_size=P, sink=S, window=W, dtype=dtype, head_class=hc, pool_slack=7, doc_len=doc_len,
                     rope_base=float(rng.choice([1.0e4, 1.0e6])))
+
+
+def random_split(seed: int, dtype: torch.dtype = torch.bfloat16) -> Workload:
+    """A random small shape with reuse and EXECUTE's head-ragged query ranges: every sequence has a
+    reused prefix; GLOBAL heads recompute from 0 (most sequences) or from a point inside the prefix."""
+    rng = np.random.Generator(np.random.PCG64(5000 + seed))
+    wl = random_small(seed, dtype, allow_reuse=True)
+    qs = [int(rng.integers(1, L)) if L > 1 else 0 for L in wl.kv_lens]
+    qg = [0 if rng.random() < 0.7 or s == 0 else int(rng.integers(0, s + 1)) for s in qs]
+    hc = wl.head_class.copy()
+    if wl.num_kv_heads > 1:  # both classes present
+        hc[0, 0], hc[0, 1] = GLOBAL, LOCAL
+    wl = dataclasses.replace(wl, q_starts=qs, head_class=hc, name="random-split seed %d" % seed,
+                             config_id=300 + seed)
+    return execute_split(wl, qg, name=wl.name)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -279,7 +322,7 @@ def make_inputs(wl: Workload, device: str | torch.device = "cpu", num_pages: Opt
     cu = wl.cu_q()
     if wl.boost_frac > 0:
         for b in range(wl.num_seqs):
-            qs = wl.q_starts[b]
+            qs = wl.q_begin(b)
             rows = torch.from_numpy(boost[b][:, qs:].T.copy()).to(k_new.device)  # [q_len][Hkv]
             blk = k_new[cu[b]:cu[b + 1]]
             blk[rows] = blk[rows] * 4
