@@ -132,7 +132,9 @@ struct rk_tables {
   int32_t layer_begin = 0, layer_end = 0, num_seqs = 0, H = 0, Hkv = 0, G = 0, T = 0, P = 0, D = 0;
   int32_t elem_bytes = 2;
   int32_t sink = 0, window = 1;
-  std::vector<int32_t> q_start, kv_len, cu_q;
+  // q_start: the LOCAL heads' first query position; q_begin: the GLOBAL heads' (<= q_start), where
+  // a sequence's packed rows begin
+  std::vector<int32_t> q_start, q_begin, kv_len, cu_q;
   std::vector<uint8_t> head_class;  // [num_layers * Hkv]
   // held pages per key k = ((l - layer_begin) * Hkv + g) * num_seqs + b, logical pages ascending
   std::vector<int64_t> held_off;
@@ -160,6 +162,7 @@ struct rk_tables {
     return ((int64_t)(l - layer_begin) * Hkv + g) * num_seqs + b;
   }
   int32_t n_logical(int32_t b) const { return (int32_t)ceil_div(kv_len[b], P); }
+  int32_t class_start(int cls, int32_t b) const { return cls == RK_GLOBAL ? q_begin[b] : q_start[b]; }
 };
 
 namespace {
@@ -170,6 +173,11 @@ struct WsLayout {
   std::vector<size_t> page_base, page_ids, head_class, items, app;
   size_t total = 0;
 };
+
+// first packed position of sequence b: the GLOBAL heads' start
+int32_t batch_q_begin(const rk_batch_desc *bd, int32_t b) {
+  return bd->q_start_global ? bd->q_start_global[b] : bd->q_start[b];
+}
 
 rk_status check_batch(const rk_pool *pool, const rk_batch_desc *bd) {
   if (!pool || !bd) return fail(RK_ERR_INVALID_ARG, "null pool or batch");
@@ -192,7 +200,10 @@ rk_status check_batch(const rk_pool *pool, const rk_batch_desc *bd) {
     if (bd->kv_len[b] < 0 || bd->q_start[b] < 0 || bd->q_start[b] > bd->kv_len[b])
       return fail(RK_ERR_INVALID_ARG, "seq %d: need 0 <= q_start (%d) <= kv_len (%d)", b, bd->q_start[b],
                   bd->kv_len[b]);
-    total_q += bd->kv_len[b] - bd->q_start[b];
+    if (bd->q_start_global && (bd->q_start_global[b] < 0 || bd->q_start_global[b] > bd->q_start[b]))
+      return fail(RK_ERR_INVALID_ARG, "seq %d: need 0 <= q_start_global (%d) <= q_start (%d)", b,
+                  bd->q_start_global[b], bd->q_start[b]);
+    total_q += bd->kv_len[b] - batch_q_begin(bd, b);
   }
   if (total_q > INT32_MAX) return fail(RK_ERR_UNSUPPORTED, "more than 2^31 query tokens");
   for (int64_t i = 0; i < (int64_t)pd.num_layers * pd.num_kv_heads; ++i)
@@ -210,7 +221,7 @@ WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd) {
   int32_t T = rk::kRowsPerItem / G;
   int64_t n_logical = 0, n_items = 0, n_app = 0;
   for (int32_t b = 0; b < bd->num_seqs; ++b) {
-    int32_t L = bd->kv_len[b], qs = bd->q_start[b];
+    int32_t L = bd->kv_len[b], qs = batch_q_begin(bd, b);
     n_logical += ceil_div(L, pd.page_size);
     n_items += ceil_div(L - qs, T);
     if (L > qs) n_app += (L - 1) / pd.page_size - qs / pd.page_size + 1;
@@ -257,17 +268,17 @@ void schedule_layer(const rk_tables &t, int32_t l, std::vector<rk::Item> &items)
     if (t.head_class[(size_t)l * t.Hkv + g] == RK_GLOBAL)
       for (int32_t b = 0; b < t.num_seqs; ++b) global_kv_bytes += (int64_t)t.kv_len[b] * t.D * 2 * t.elem_bytes;
   if (global_kv_bytes <= kSharedCacheBytes) {
-    for (int32_t b = 0; b < t.num_seqs; ++b) {
-      int32_t qs = t.q_start[b], nq = t.kv_len[b] - t.q_start[b];
+    for (int32_t b = 0; b < t.num_seqs; ++b)
       for (int32_t g = 0; g < t.Hkv; ++g) {
         int cls = t.head_class[(size_t)l * t.Hkv + g];
+        // the head's rows: positions class_start .. kv_len - 1, packed rows from q_begin
+        const int32_t qs = t.class_start(cls, b), row0 = qs - t.q_begin[b], nq = t.kv_len[b] - qs;
         for (int32_t tok0 = 0; tok0 < nq; tok0 += t.T) {
           int32_t tok1 = std::min(nq, tok0 + t.T);
           rk::TileRange r = rk::tile_range(cls, qs + tok0, qs + tok1 - 1, t.sink, t.window);
-          items.push_back({b, g, tok0, r.count()});
+          items.push_back({b, g, row0 + tok0, r.count()});
         }
       }
-    }
     std::stable_sort(items.begin(), items.end(), [](const rk::Item &a, const rk::Item &b) { return a.tiles > b.tiles; });
     return;
   }
@@ -275,14 +286,14 @@ void schedule_layer(const rk_tables &t, int32_t l, std::vector<rk::Item> &items)
   int64_t total = 0;
   std::vector<rk::Item> grp;
   for (int32_t b = 0; b < t.num_seqs; ++b) {
-    int32_t qs = t.q_start[b], nq = t.kv_len[b] - t.q_start[b];
     for (int32_t g = 0; g < t.Hkv; ++g) {
       int cls = t.head_class[(size_t)l * t.Hkv + g];
+      const int32_t qs = t.class_start(cls, b), row0 = qs - t.q_begin[b], nq = t.kv_len[b] - qs;
       grp.clear();
       for (int32_t tok0 = 0; tok0 < nq; tok0 += t.T) {
         int32_t tok1 = std::min(nq, tok0 + t.T);
         rk::TileRange r = rk::tile_range(cls, qs + tok0, qs + tok1 - 1, t.sink, t.window);
-        grp.push_back({b, g, tok0, r.count()});
+        grp.push_back({b, g, row0 + tok0, r.count()});
         total += r.count();
       }
       if (!grp.empty()) runs.push_back(grp);
@@ -398,9 +409,11 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
   t->sink = bd->sink;
   t->window = bd->window;
   t->q_start.assign(bd->q_start, bd->q_start + bd->num_seqs);
+  t->q_begin.resize(bd->num_seqs);
+  for (int32_t b = 0; b < bd->num_seqs; ++b) t->q_begin[b] = batch_q_begin(bd, b);
   t->kv_len.assign(bd->kv_len, bd->kv_len + bd->num_seqs);
   t->cu_q.resize(bd->num_seqs + 1, 0);
-  for (int32_t b = 0; b < bd->num_seqs; ++b) t->cu_q[b + 1] = t->cu_q[b] + (t->kv_len[b] - t->q_start[b]);
+  for (int32_t b = 0; b < bd->num_seqs; ++b) t->cu_q[b + 1] = t->cu_q[b] + (t->kv_len[b] - t->q_begin[b]);
   t->head_class.assign(bd->head_class, bd->head_class + (size_t)pd.num_layers * pd.num_kv_heads);
 
   // held pages of every (layer, kv head, seq), in allocation order
@@ -443,7 +456,7 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
     }
     std::vector<int32_t> &app = t->app_items[l - bd->layer_begin];
     for (int32_t b = 0; b < t->num_seqs; ++b) {
-      int32_t qs = t->q_start[b], L = t->kv_len[b];
+      int32_t qs = t->q_begin[b], L = t->kv_len[b];  // pages from the earliest class start
       if (L <= qs) continue;
       for (int32_t p = qs / t->P; p <= (L - 1) / t->P; ++p) {
         app.push_back(b);
@@ -463,7 +476,7 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
     for (int32_t g = 0; g < t->Hkv; ++g) {
       int cls = t->head_class[(size_t)l * t->Hkv + g];
       for (int32_t b = 0; b < t->num_seqs; ++b) {
-        int64_t v = (int64_t)t->G * visible_pairs(cls, t->q_start[b], t->kv_len[b], t->sink, t->window);
+        int64_t v = (int64_t)t->G * visible_pairs(cls, t->class_start(cls, b), t->kv_len[b], t->sink, t->window);
         s.visible_pairs += v;
         if (cls == RK_GLOBAL) s.visible_pairs_global += v;
       }
@@ -494,7 +507,7 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
     std::memset(h, 0, ws.total);
     rk::SeqInfo *seqs = reinterpret_cast<rk::SeqInfo *>(h + ws.seqs);
     for (int32_t b = 0; b < t->num_seqs; ++b)
-      seqs[b] = {t->q_start[b], t->kv_len[b], t->cu_q[b], t->kv_len[b] - t->q_start[b]};
+      seqs[b] = {t->q_begin[b], t->kv_len[b], t->cu_q[b], t->kv_len[b] - t->q_begin[b], t->q_start[b]};
     char *dbase = static_cast<char *>(d_ws);
     t->d_seqs = reinterpret_cast<const rk::SeqInfo *>(dbase + ws.seqs);
     t->dev.resize(nl);
@@ -558,6 +571,7 @@ rk::KvWriteParams kv_params(const rk_pool *pool, const rk_tables *t, int32_t lay
   p.page_base = d.page_base;
   p.page_ids = d.page_ids;
   p.seqs = t->d_seqs;
+  p.head_class = d.head_class;
   p.num_seqs = t->num_seqs;
   p.Hkv = t->Hkv;
   p.P = t->P;

@@ -20,10 +20,11 @@ constexpr int kKeyTile = 64;
 constexpr int kThreads = 256;
 
 struct SeqInfo {
-  int32_t q_start;
+  int32_t q_start;        // position of the sequence's first packed row (the GLOBAL heads' start)
   int32_t kv_len;
-  int32_t cu_q;  // first packed query row of the sequence
-  int32_t n_q;   // kv_len - q_start
+  int32_t cu_q;           // first packed query row of the sequence
+  int32_t n_q;            // kv_len - q_start
+  int32_t q_start_local;  // first query position of the LOCAL heads (>= q_start)
 };
 
 struct Item {
@@ -92,6 +93,7 @@ struct KvWriteParams {
   const int32_t *page_ids;
   const SeqInfo *seqs;
   const int32_t *app_items;  // append: [n][2] = (seq, logical page)
+  const uint8_t *head_class; // append: [Hkv] classes of the layer
   int32_t n_items;
   int32_t num_seqs;
   int32_t Hkv;

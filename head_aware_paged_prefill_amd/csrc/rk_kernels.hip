@@ -599,7 +599,9 @@ __global__ void __launch_bounds__(256) kv_write(KvWriteParams p) {
     seq = p.app_items[2 * blockIdx.x];
     lp = p.app_items[2 * blockIdx.x + 1];
     si = p.seqs[seq];
-    t_lo = max(lp * P, si.q_start);
+    // a GLOBAL head writes from the sequence's first packed position, a LOCAL head from its own
+    // (later) start: below it the head keeps its reused KV
+    t_lo = max(lp * P, p.head_class[g] == RK_GLOBAL ? si.q_start : si.q_start_local);
     t_hi = min(lp * P + P, si.kv_len);
   }
   const int pg = p.page_ids[p.page_base[g * p.num_seqs + seq] + lp];

@@ -53,7 +53,8 @@ class BatchDesc(ctypes.Structure):
     _fields_ = [("layer_begin", ctypes.c_int32), ("layer_end", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("num_q_heads", ctypes.c_int32), ("q_start", ctypes.POINTER(ctypes.c_int32)),
                 ("kv_len", ctypes.POINTER(ctypes.c_int32)), ("head_class", ctypes.POINTER(ctypes.c_uint8)),
-                ("sink", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("q_start_global", ctypes.POINTER(ctypes.c_int32))]
 
 
 class TablesStats(ctypes.Structure):
@@ -198,28 +199,37 @@ class Tables:
         self.workspace = workspace
 
 
-def _batch(pool: Pool, layer_begin, layer_end, num_q_heads, q_start, kv_len, head_class, sink, window):
+def _batch(pool: Pool, layer_begin, layer_end, num_q_heads, q_start, kv_len, head_class, sink, window,
+           q_start_global=None):
     qs, kl = _i32(q_start), _i32(kv_len)
     hc = np.ascontiguousarray(np.asarray(head_class, dtype=np.uint8).reshape(-1))
+    qg = None if q_start_global is None else _i32(q_start_global)
+    if qg is not None and len(qg) != len(qs):
+        raise ValueError("q_start_global needs one entry per sequence")
     b = BatchDesc(layer_begin, layer_end, len(qs), num_q_heads,
                   qs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), kl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                  hc.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), sink, window)
-    return b, (qs, kl, hc)
+                  hc.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), sink, window,
+                  None if qg is None else qg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    return b, (qs, kl, hc, qg)
 
 
 def rk_seg_tables_workspace_bytes(pool: Pool, layer_begin, layer_end, num_q_heads, q_start, kv_len, head_class,
-                                  sink, window) -> int:
-    b, keep = _batch(pool, layer_begin, layer_end, num_q_heads, q_start, kv_len, head_class, sink, window)
+                                  sink, window, q_start_global=None) -> int:
+    b, keep = _batch(pool, layer_begin, layer_end, num_q_heads, q_start, kv_len, head_class, sink, window,
+                     q_start_global)
     n = ctypes.c_size_t()
     _check(load().rk_seg_tables_workspace_bytes(pool.handle, ctypes.byref(b), ctypes.byref(n)))
     return n.value
 
 
 def rk_seg_build_tables(pool: Pool, layer_begin: int, layer_end: int, num_q_heads: int, q_start, kv_len,
-                        head_class, sink: int, window: int, device=True, workspace=None, stream=None) -> Tables:
+                        head_class, sink: int, window: int, device=True, workspace=None, stream=None,
+                        q_start_global=None) -> Tables:
     """Build the tables; with device=True a uint8 workspace tensor is allocated on the current device
-    (or `workspace` is used) and the tables are uploaded into it on the stream."""
-    b, keep = _batch(pool, layer_begin, layer_end, num_q_heads, q_start, kv_len, head_class, sink, window)
+    (or `workspace` is used) and the tables are uploaded into it on the stream.  q_start_global
+    (optional, per sequence, <= q_start): the GLOBAL heads' first query position."""
+    b, keep = _batch(pool, layer_begin, layer_end, num_q_heads, q_start, kv_len, head_class, sink, window,
+                     q_start_global)
     L = load()
     ws_ptr, ws_bytes, st = None, 0, None
     if device:

@@ -47,11 +47,12 @@ class PrefillRunner:
         le = lb + 1 if layer_end is None else layer_end
         if self.workspace is None:
             nbytes = rk_seg.rk_seg_tables_workspace_bytes(self.pool, lb, le, wl.num_q_heads, wl.q_starts, wl.kv_lens,
-                                                          wl.head_class, wl.sink, wl.window)
+                                                          wl.head_class, wl.sink, wl.window, wl.q_starts_global)
             self.workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=self.device)
         self.tables = rk_seg.rk_seg_build_tables(self.pool, lb, le, wl.num_q_heads, wl.q_starts, wl.kv_lens,
                                                  wl.head_class, wl.sink, wl.window, device=True,
-                                                 workspace=self.workspace, stream=stream)
+                                                 workspace=self.workspace, stream=stream,
+                                                 q_start_global=wl.q_starts_global)
         return self.tables
 
     def import_docs(self, docs, layer: Optional[int] = None, rope_style: int = rk_seg.RK_ROPE_ROTATE_HALF, stream=None):

@@ -28,15 +28,24 @@
  *   q, o      [total_q][num_q_heads][head_dim]   queries packed by sequence, in sequence order
  *   k_new, v_new [total_q][num_kv_heads][head_dim]  keys/values of the query tokens
  *   lse       [num_q_heads][total_q] fp32, natural log
- * where sequence b contributes kv_len[b] - q_start[b] query tokens at absolute
- * positions q_start[b] .. kv_len[b]-1.  Element type: RK_BF16 (bfloat16) or RK_F32.
+ * where sequence b contributes kv_len[b] - qb[b] rows for absolute positions
+ * qb[b] .. kv_len[b]-1, with qb[b] = q_start_global[b] when the batch gives it and
+ * q_start[b] otherwise.  Element type: RK_BF16 (bfloat16) or RK_F32.
+ *
+ * Head-ragged query ranges (EXECUTE's split: global heads recompute attention and
+ * write the online KV cache, local heads reuse theirs; page "RedKnot -
+ * Xiaohongshuが開発した…", section 使い方, EXECUTE item): a GLOBAL head computes
+ * the rows and writes the keys/values of positions q_start_global[b] ..
+ * kv_len[b]-1, a LOCAL head those of q_start[b] .. kv_len[b]-1.  Rows of a
+ * LOCAL head below q_start[b] are not written (o and lse keep their contents).
+ * Without q_start_global both classes start at q_start[b].
  * Every device pointer must be 16-byte aligned; head_dim is 64 or 128; page_size
  * is a power of two in [8, 256].
  *
  * Cache contents contract: before attention, every slot of a held page whose
  * token is below kv_len must have been written -- by the append inside
- * rk_seg_attn_prefill (tokens >= q_start) or by rk_seg_reuse_rerotate (tokens
- * below q_start).  Slots at or beyond kv_len and pages a head does not hold may
+ * rk_seg_attn_prefill (tokens from the head's class start on) or by
+ * rk_seg_reuse_rerotate (tokens below it).  Slots at or beyond kv_len and pages a head does not hold may
  * contain any bits (NaN included) before the call; the append clears the slots
  * of a sequence's last page past kv_len, and pages a head does not hold are
  * never read.  None of them reaches the output.
@@ -102,6 +111,9 @@ typedef struct {
 
 /* One prefill call over layers [layer_begin, layer_end) of a batch of sequences.
  * q_start, kv_len: host [num_seqs], 0 <= q_start[b] <= kv_len[b] < 2^31.
+ * q_start_global: host [num_seqs] or NULL; 0 <= q_start_global[b] <= q_start[b]: the first query
+ *   position of the GLOBAL heads (head-ragged query ranges, above).  NULL: q_start.
+ *   A LOCAL head holds and reads its window relative to q_start either way.
  * head_class: host [num_layers * num_kv_heads], row-major by layer, values RK_LOCAL / RK_GLOBAL.
  * sink >= 0, window >= 1.  num_q_heads must be a positive multiple of the pool's num_kv_heads.
  * All host arrays are copied. */
@@ -115,12 +127,13 @@ typedef struct {
   const uint8_t *head_class;
   int32_t sink;
   int32_t window;
+  const int32_t *q_start_global;
 } rk_batch_desc;
 
 /* Counters of one built call (host, exact integers). */
 typedef struct {
   int64_t pages_held;        /* pages the call holds over all its layers */
-  int64_t total_q;           /* query tokens per layer */
+  int64_t total_q;           /* packed query rows per layer */
   int64_t visible_pairs;     /* sum over layers, q heads and queries of |visible keys| */
   int64_t visible_pairs_global; /* the part from GLOBAL heads */
   int64_t work_items;        /* attention work items over all layers */
