@@ -7,8 +7,10 @@ attention kernel, trim local heads to sink + window and release the tables.
 
 Default workload: the Llama-3.3-70B-shaped single-GPU share (31 sequences x 32K, 64 q / 8 KV heads,
 D=128, bf16, one global KV head, sink 4, window 2048, page 16).  The line also reports the same step
-with every head global (the dense reference), the 128K Qwen3-32B-shaped call, the attention
-kernel's roofline and the fp64 oracle's rate on a bounded sample of host cores.
+with every head global (the dense reference), the 128K Qwen3-32B-shaped call, a DeepSeek-V4-Flash-
+style layer under EXECUTE's head-ragged split (global heads recompute all 128K positions, local
+heads query the last 8K), the attention kernel's roofline and the fp64 oracle's rate on a bounded
+sample of host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-extra]
 """
@@ -207,7 +209,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama70b", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the dense reference and the 128K call")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the dense reference and the two 128K calls (Qwen3-32B-shaped, EXECUTE split)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size HBM reference for counters)")
@@ -232,6 +235,10 @@ def main():
     extra = {}
     if not a.no_extra and a.workload != "qwen32b":
         extra["qwen32b_128k"] = run_workload(workloads.qwen32b(), max(2, a.steps // 2), 1, with_dense=True)
+    if not a.no_extra and a.workload != "dsv4flash_split":
+        # EXECUTE's head-ragged split: GLOBAL heads recompute all 128K positions, LOCAL heads the last 8K
+        extra["dsv4flash_execute_split_128k"] = run_workload(workloads.dsv4flash_split(3), max(2, a.steps // 2), 1,
+                                                             with_dense=True)
     cpu = None if a.no_cpu else cpu_baseline(wl, a.cpu_seconds)
     ms_attn = main_res["ms_attention"]
     achieved = main_res["tflops_attention"]
