@@ -37,7 +37,19 @@ PEAK_HBM_GBS = 8000.0
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-PROFILES = {"llama70b": "attn_bf16_llama70b_31x32K_traffic.txt", "qwen32b": "attn_bf16_qwen32b_128K_traffic.txt"}
+PROFILES = {"llama70b": "attn_bf16_llama70b_31x32K_traffic.txt", "qwen32b": "attn_bf16_qwen32b_128K_traffic.txt",
+            "dsv4flash_split": "attn_bf16_dsv4flash_split_128K_traffic.txt"}
+# what the attention launch's traffic depends on: the kernel and its work order
+KERNEL_SOURCES = ["head_aware_paged_prefill_amd/csrc/rk_attn.hip", "head_aware_paged_prefill_amd/csrc/rk_sched.cpp",
+                  "head_aware_paged_prefill_amd/csrc/rk_sched.h", "head_aware_paged_prefill_amd/csrc/rk_internal.h",
+                  "head_aware_paged_prefill_amd/csrc/rk_device.h"]
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
@@ -48,10 +60,7 @@ def measured_traffic(workload: str):
     if not path or not os.path.exists(path):
         return None
     kv = dict(line.strip().split("=", 1) for line in open(path) if "=" in line and not line.startswith(" "))
-    h = hashlib.sha256()
-    for f in kv.get("kernel_sources", "").split(","):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != kv.get("kernel_sources_sha256"):
+    if kv.get("kernel_sources", "").split(",") != KERNEL_SOURCES or kv.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None
     return int(kv["traffic_bytes_per_launch"])
 

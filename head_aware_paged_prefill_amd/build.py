@@ -35,16 +35,24 @@ def _run(cmd, verbose):
     return r
 
 
+HOST_SOURCES = ["rk_host.cpp", "rk_sched.cpp"]
+HIP_SOURCES = ["rk_attn.hip", "rk_kernels.hip"]
+
+
 def build(verbose: bool = False, out: str = LIB, extra_hip: list | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     inc = ["-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
-    host_o = os.path.join(BUILD, "rk_host.o")
-    kern_o = os.path.join(BUILD, "rk_kernels.o")
-    _run(["g++"] + HOST_FLAGS + inc + ["-c", os.path.join(CSRC, "rk_host.cpp"), "-o", host_o], verbose)
-    _run([HIPCC] + HIP_FLAGS + (extra_hip or []) + inc + ["-c", os.path.join(CSRC, "rk_kernels.hip"), "-o", kern_o],
-         verbose)
+    objs = []
+    for src in HOST_SOURCES:
+        o = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        _run(["g++"] + HOST_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", o], verbose)
+        objs.append(o)
+    for src in HIP_SOURCES:
+        o = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        _run([HIPCC] + HIP_FLAGS + (extra_hip or []) + inc + ["-c", os.path.join(CSRC, src), "-o", o], verbose)
+        objs.append(o)
     tmp = out + ".tmp"
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", host_o, kern_o, "-o", tmp], verbose)
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 
