@@ -154,3 +154,44 @@ def prefill_rows(inp, seq: int, q_head: int, rows, scale: Optional[float] = None
         scale = 1.0 / np.sqrt(wl.head_dim)
     mask = attention.visibility_mask(cls, wl.q_begin(seq) + rows, wl.kv_lens[seq], wl.sink, wl.window)
     return attention.masked_attention(q, k, v, mask, scale)
+
+
+def kv_offsets(wl):
+    """Start of each sequence's keys in the packed per-key output: cumulative kv_len."""
+    out = [0]
+    for L in wl.kv_lens:
+        out.append(out[-1] + L)
+    return out
+
+
+def key_mass(inp, scale: Optional[float] = None, rope_style: int = rope.ROTATE_HALF):
+    """Per-key attention mass: mass [H][sum kv_len] (fp64), mass[h][off_b + j] = the sum, over the call's
+    queries i of head h (from its class start), of the attention weight p_ij of key j.
+
+    This is the attention-score signal by which the pages route tokens: the dense FFN runs only on the
+    top-k tokens by attention score, the rest take the residual path ([ZC] 事件内容, item 2; [SS]
+    RedKnot技术原理, 3. 稀疏FFN动态调度).  Which statistic of the scores ranks a token is not stated;
+    the plainest reading is the attention a token receives as a key, per head.  Each row of p sums
+    to one, so a head's masses sum to its number of query rows."""
+    wl = inp.wl
+    if scale is None:
+        scale = 1.0 / np.sqrt(wl.head_dim)
+    off = kv_offsets(wl)
+    mass = np.zeros((wl.num_q_heads, off[-1]))
+    cu = wl.cu_q()
+    kv_class = wl.head_class[wl.layer]
+    for b in range(wl.num_seqs):
+        L, qb = wl.kv_lens[b], wl.q_begin(b)
+        q = to64(inp.q[cu[b]:cu[b + 1]])  # [rows][H][D]
+        kv = [head_kv(inp, b, g, rope_style) for g in range(wl.num_kv_heads)]
+        for h in range(wl.num_q_heads):
+            g = h // wl.group
+            cls = int(kv_class[g])
+            a = wl.q_start_of(b, cls)
+            if a >= L:
+                continue
+            pos = np.arange(a, L)
+            p = attention.softmax_rows(q[a - qb:, h], kv[g][0], attention.visibility_mask(cls, pos, L, wl.sink,
+                                                                                          wl.window), scale)
+            mass[h, off[b]:off[b] + L] = p.sum(axis=0)
+    return mass
