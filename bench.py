@@ -123,6 +123,32 @@ class Bench:
         return (t1 - t0) * 1e3 / steps
 
 
+def time_key_mass(b: "Bench", reps: int) -> dict:
+    """Time the per-key attention mass pass (rk_seg_key_mass) after one attention call on the same
+    tables; useful work is the QK half: 2 * D flops per visible pair."""
+    wl, r = b.wl, b.r
+    r.build()
+    r.import_docs(b.inp.docs)
+    rk_seg.rk_seg_append_kv(r.tables, wl.layer, b.inp.k_new, b.inp.v_new)
+    rk_seg.rk_seg_attn_prefill(r.tables, wl.layer, b.inp.q, None, None, b.o, b.lse)
+    mass = torch.empty((wl.num_q_heads, sum(wl.kv_lens)), dtype=torch.float32, device="cuda")
+    rk_seg.rk_seg_key_mass(r.tables, wl.layer, b.inp.q, b.lse, mass)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rk_seg.rk_seg_key_mass(r.tables, wl.layer, b.inp.q, b.lse, mass)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    stats = rk_seg.rk_seg_tables_stats(r.tables)
+    r.release(trim=True)
+    del mass
+    ms = float(np.mean(ts))
+    tf = 2.0 * wl.head_dim * stats["visible_pairs"] / (ms * 1e-3) / 1e12
+    return {"ms": ms, "tflops": tf, "pct_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS}
+
+
 def run_workload(wl, steps: int, warmup: int, with_dense: bool):
     log("workload: %s" % wl.name)
     inp = workloads.make_inputs(wl, device="cuda")
@@ -147,6 +173,10 @@ def run_workload(wl, steps: int, warmup: int, with_dense: bool):
     res["pct_mfma_peak_attention"] = 100.0 * res["tflops_attention"] / PEAK_BF16_TFLOPS
     log("  mixed: %.3f ms/step, attention %.3f ms, %.1f useful TFLOP/s (%.1f%% of bf16 peak)" % (
         ms_step, res["ms_attention"], res["tflops_attention"], res["pct_mfma_peak_attention"]))
+    if wl.group <= 16 and wl.dtype == torch.bfloat16:
+        res["key_mass"] = time_key_mass(b, max(2, steps // 2))
+        log("  per-key mass pass: %.3f ms, %.1f useful TFLOP/s (QK half, %.1f%% of bf16 peak)" % (
+            res["key_mass"]["ms"], res["key_mass"]["tflops"], res["key_mass"]["pct_mfma_peak"]))
     if with_dense:
         wl_d = wl.with_classes(np.ones_like(wl.head_class), wl.name + " all-global")
         bd = Bench(wl_d, dataclasses.replace(inp, wl=wl_d), runner)

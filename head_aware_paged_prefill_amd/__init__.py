@@ -8,5 +8,5 @@ from . import rk_seg  # noqa: F401
 from .rk_seg import (RK_BF16, RK_F32, RK_GLOBAL, RK_LOCAL, RkError, load, rk_seg_append_kv,  # noqa: F401
                      rk_seg_attn_prefill, rk_seg_build_tables, rk_seg_pool_create, rk_seg_pool_destroy,
                      rk_seg_pool_free_list, rk_seg_pool_query, rk_seg_reuse_rerotate, rk_seg_tables_destroy,
-                     rk_seg_tables_export, rk_seg_tables_schedule, rk_seg_tables_stats, rk_seg_tables_trim,
+                     rk_seg_tables_export, rk_seg_tables_mass_schedule, rk_seg_tables_schedule, rk_seg_tables_stats, rk_seg_tables_trim,
                      rk_seg_tables_workspace_bytes, rk_seg_version)

@@ -43,30 +43,6 @@ constexpr int BN = kKeyTile;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest un-normalised weight allowed
 
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
-
-__device__ __forceinline__ int swap_bits23(int j) { return (j & ~0xC) | ((j & 4) << 1) | ((j & 8) >> 1); }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ bool visible(int cls, int i, int j, int sink, int window) {
-  return j <= i && (cls == RK_GLOBAL || j < sink || j > i - window);
-}
-
 // ------------------------------------------------------------------------------------------------
 // bf16 attention
 // ------------------------------------------------------------------------------------------------
@@ -90,35 +66,8 @@ struct AttnBf16Smem {
   bf16_t v[2][TPS][D * BN];
 };
 
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
 __device__ __forceinline__ int vswz(int d, int Pt) {
   return (d / (128 / Pt)) & (Pt / 8 - 1);
-}
-
-// max / sum of a value over the two half-waves (lanes l and l ^ 32)
-__device__ __forceinline__ float halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// The value unchanged, hidden from code motion: a loop-invariant 32-bit lane offset then stays
-// 32-bit at its use, where it forms the scalar-base + 32-bit-offset address of a global load
-// (instead of a hoisted 64-bit vector address that holds two registers for the whole loop).
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-__device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_block) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
-                                   (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
 }
 
 // One work item = 256 query rows; eight waves of 32 rows (one query column of S^T per lane).

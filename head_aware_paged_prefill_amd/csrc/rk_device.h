@@ -1,8 +1,10 @@
-// Device-side vector types shared by the gfx950 kernels of the library.
+// Device-side vector types and small helpers shared by the gfx950 kernels of the library.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "rk_seg.h"
 
 namespace rk {
 
@@ -13,5 +15,60 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+__device__ __forceinline__ int swap_bits23(int j) { return (j & ~0xC) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ bool visible(int cls, int i, int j, int sink, int window) {
+  return j <= i && (cls == RK_GLOBAL || j < sink || j > i - window);
+}
+
+// Swizzle of the 16-byte chunks of a row of D bf16 values staged in LDS by direct 16-byte loads:
+// chunk c of row r sits in slot c ^ kswz(r), so 16 consecutive lanes reading 16 consecutive rows at
+// one chunk index touch 16 distinct 16-byte slots of every 256-byte bank window.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// max / sum of a value over the two half-waves (lanes l and l ^ 32)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The value unchanged, hidden from code motion: a loop-invariant 32-bit lane offset then stays
+// 32-bit at its use, where it forms the scalar-base + 32-bit-offset address of a global load
+// (instead of a hoisted 64-bit vector address that holds two registers for the whole loop).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_block) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
+                                   (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
+}
 
 }  // namespace rk

@@ -142,6 +142,7 @@ struct rk_tables {
   std::vector<int32_t> held_logical, held_phys;
   std::vector<std::vector<rk::Item>> items;     // per layer of the call, in launch order
   std::vector<std::vector<int32_t>> app_items;  // per layer: (seq, logical page) pairs
+  std::vector<std::vector<rk::MassUnit>> mass_units;  // per layer: per-key mass work units, launch order
   // device view
   void *d_ws = nullptr;
   size_t ws_used = 0;
@@ -151,6 +152,7 @@ struct rk_tables {
     const uint8_t *head_class;
     const rk::Item *items;
     const int32_t *app;
+    const rk::MassUnit *mass_units;
   };
   std::vector<LayerDev> dev;
   const rk::SeqInfo *d_seqs = nullptr;
@@ -171,7 +173,7 @@ namespace {
 // Device workspace layout of one build.  Offsets are relative to the workspace base.
 struct WsLayout {
   size_t seqs = 0;
-  std::vector<size_t> page_base, page_ids, head_class, items, app;
+  std::vector<size_t> page_base, page_ids, head_class, items, app, mass;
   size_t total = 0;
 };
 
@@ -212,9 +214,14 @@ rk_status check_batch(const rk_pool *pool, const rk_batch_desc *bd) {
   return RK_OK;
 }
 
-WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd) {
+// The per-key mass units of each layer are scheduled here (their count sizes the workspace) and
+// returned in *mass_units when it is not null.
+WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, std::vector<std::vector<rk::MassUnit>> *mass_units) {
   const rk_pool_desc &pd = pool->desc;
   WsLayout w;
+  std::vector<int32_t> q_begin(std::max(1, bd->num_seqs));
+  for (int32_t b = 0; b < bd->num_seqs; ++b) q_begin[b] = batch_q_begin(bd, b);
+  if (mass_units) mass_units->assign(bd->layer_end - bd->layer_begin, {});
   size_t off = 0;
   w.seqs = off;
   off = align_up(off + sizeof(rk::SeqInfo) * std::max(1, bd->num_seqs));
@@ -239,6 +246,14 @@ WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd) {
     off = align_up(off + sizeof(rk::Item) * std::max<int64_t>(1, n_items * pd.num_kv_heads * kXcd));
     w.app.push_back(off);
     off = align_up(off + 2 * sizeof(int32_t) * std::max<int64_t>(1, n_app));
+    rk::SchedInput si{bd->num_seqs, pd.num_kv_heads, T, pd.head_dim, pd.dtype == RK_F32 ? 4 : 2, bd->sink, bd->window,
+                      &bd->head_class[(size_t)l * pd.num_kv_heads], bd->kv_len, bd->q_start, q_begin.data()};
+    // sized by a bound that does not depend on the head classes, so that one workspace serves
+    // every layer of a model
+    const int32_t mk = rk::mass_keys_per_unit(G), mt = rk::mass_tokens_per_step(G);
+    if (mass_units && G <= 16) rk::mass_schedule(si, mk, mt, (*mass_units)[l - bd->layer_begin]);
+    w.mass.push_back(off);
+    off = align_up(off + sizeof(rk::MassUnit) * std::max<int64_t>(1, G <= 16 ? rk::mass_units_bound(si, mk, mt) : 0));
   }
   w.total = off;
   return w;
@@ -289,7 +304,8 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
   rk_status st = check_batch(pool, bd);
   if (st != RK_OK) return st;
   const rk_pool_desc &pd = pool->desc;
-  WsLayout ws = plan_ws(pool, bd);
+  std::vector<std::vector<rk::MassUnit>> mass_units;
+  WsLayout ws = plan_ws(pool, bd, &mass_units);
   if (d_ws) {
     if ((reinterpret_cast<uintptr_t>(d_ws) & (kAlign - 1)) != 0)
       return fail(RK_ERR_INVALID_ARG, "workspace not 256-byte aligned");
@@ -299,6 +315,7 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
 
   std::unique_ptr<rk_tables> t(new rk_tables());
   t->pool = pool;
+  t->mass_units = std::move(mass_units);
   t->layer_begin = bd->layer_begin;
   t->layer_end = bd->layer_end;
   t->num_seqs = bd->num_seqs;
@@ -411,8 +428,12 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
     char *h = static_cast<char *>(t->staging.ptr);
     std::memset(h, 0, ws.total);
     rk::SeqInfo *seqs = reinterpret_cast<rk::SeqInfo *>(h + ws.seqs);
-    for (int32_t b = 0; b < t->num_seqs; ++b)
-      seqs[b] = {t->q_begin[b], t->kv_len[b], t->cu_q[b], t->kv_len[b] - t->q_begin[b], t->q_start[b]};
+    int64_t kv_off = 0;  // per-key outputs need it below 2^31 (checked where they are computed)
+    for (int32_t b = 0; b < t->num_seqs; ++b) {
+      seqs[b] = {t->q_begin[b], t->kv_len[b], t->cu_q[b], t->kv_len[b] - t->q_begin[b], t->q_start[b],
+                 (int32_t)std::min<int64_t>(kv_off, INT32_MAX)};
+      kv_off += t->kv_len[b];
+    }
     char *dbase = static_cast<char *>(d_ws);
     t->d_seqs = reinterpret_cast<const rk::SeqInfo *>(dbase + ws.seqs);
     t->dev.resize(nl);
@@ -433,11 +454,13 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
       std::memcpy(h + ws.head_class[li], &t->head_class[(size_t)l * t->Hkv], t->Hkv);
       std::memcpy(h + ws.items[li], t->items[li].data(), sizeof(rk::Item) * t->items[li].size());
       std::memcpy(h + ws.app[li], t->app_items[li].data(), sizeof(int32_t) * t->app_items[li].size());
+      std::memcpy(h + ws.mass[li], t->mass_units[li].data(), sizeof(rk::MassUnit) * t->mass_units[li].size());
       t->dev[li] = {reinterpret_cast<const int32_t *>(dbase + ws.page_base[li]),
                     reinterpret_cast<const int32_t *>(dbase + ws.page_ids[li]),
                     reinterpret_cast<const uint8_t *>(dbase + ws.head_class[li]),
                     reinterpret_cast<const rk::Item *>(dbase + ws.items[li]),
-                    reinterpret_cast<const int32_t *>(dbase + ws.app[li])};
+                    reinterpret_cast<const int32_t *>(dbase + ws.app[li]),
+                    reinterpret_cast<const rk::MassUnit *>(dbase + ws.mass[li])};
     }
     hipStream_t sm = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(d_ws, h, ws.total, hipMemcpyHostToDevice, sm);
@@ -598,7 +621,7 @@ rk_status rk_seg_tables_workspace_bytes(const rk_pool *pool, const rk_batch_desc
   if (!bytes) return fail(RK_ERR_INVALID_ARG, "null bytes");
   rk_status st = check_batch(pool, batch);
   if (st != RK_OK) return st;
-  *bytes = plan_ws(pool, batch).total;
+  *bytes = plan_ws(pool, batch, nullptr).total;
   return RK_OK;
   RK_GUARD_END
 }
@@ -651,6 +674,26 @@ rk_status rk_seg_tables_schedule(const rk_tables *t, int32_t layer, int32_t *ite
       items[4 * i + 1] = v[i].kv_head;
       items[4 * i + 2] = v[i].tok0;
       items[4 * i + 3] = v[i].tiles;
+    }
+  return RK_OK;
+}
+
+rk_status rk_seg_tables_mass_schedule(const rk_tables *t, int32_t layer, int32_t *units, int64_t cap,
+                                      int64_t *n_units, int32_t *keys_per_unit, int32_t *tokens_per_step,
+                                      int32_t *steps_per_chunk) {
+  if (!t) return fail(RK_ERR_INVALID_ARG, "null tables");
+  if (layer < t->layer_begin || layer >= t->layer_end) return fail(RK_ERR_INVALID_ARG, "layer outside the tables");
+  const std::vector<rk::MassUnit> &v = t->mass_units[layer - t->layer_begin];
+  if (n_units) *n_units = (int64_t)v.size();
+  if (keys_per_unit) *keys_per_unit = rk::mass_keys_per_unit(t->G);
+  if (steps_per_chunk) *steps_per_chunk = rk::kMassChunkSteps;
+  if (tokens_per_step) *tokens_per_step = rk::mass_tokens_per_step(t->G);
+  if (units)
+    for (int64_t i = 0; i < std::min<int64_t>(cap, (int64_t)v.size()); ++i) {
+      units[4 * i + 0] = v[i].seq;
+      units[4 * i + 1] = v[i].kv_head;
+      units[4 * i + 2] = v[i].kblk;
+      units[4 * i + 3] = v[i].qc;
     }
   return RK_OK;
 }
@@ -803,6 +846,55 @@ rk_status rk_seg_attn_prefill(rk_pool *pool, const rk_tables *t, int32_t layer, 
   p.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = rk::launch_attention(p, pool->desc.dtype, pool->desc.head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return RK_OK;
+  RK_GUARD_END
+}
+
+rk_status rk_seg_key_mass(rk_pool *pool, const rk_tables *t, int32_t layer, const void *q, const float *lse,
+                          float *mass, float softmax_scale, void *stream) {
+  RK_GUARD_BEGIN
+  rk_status st = check_device_tables(pool, t, layer);
+  if (st != RK_OK) return st;
+  if (pool->desc.dtype != RK_BF16) return fail(RK_ERR_UNSUPPORTED, "per-key mass needs a bf16 pool");
+  if (t->G > 16) return fail(RK_ERR_UNSUPPORTED, "per-key mass supports at most 16 q heads per KV head");
+  const int64_t total_q = t->cu_q[t->num_seqs];
+  int64_t total_kv = 0;
+  for (int32_t b = 0; b < t->num_seqs; ++b) total_kv += t->kv_len[b];
+  if (total_kv > INT32_MAX) return fail(RK_ERR_UNSUPPORTED, "more than 2^31 keys in the call");
+  if (total_kv == 0) return RK_OK;
+  if (!mass || (reinterpret_cast<uintptr_t>(mass) & 3u)) return fail(RK_ERR_INVALID_ARG, "mass null or not 4-byte aligned");
+  if (total_q > 0 && (!q || !aligned16(q) || !lse || (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(RK_ERR_INVALID_ARG, "q / lse null or misaligned");
+  if (!(softmax_scale <= 0.0f) && !std::isfinite(softmax_scale)) return fail(RK_ERR_INVALID_ARG, "softmax_scale not finite");
+  const rk_tables::LayerDev &d = t->dev[layer - t->layer_begin];
+  rk::MassParams p{};
+  p.q = q;
+  p.lse = lse;
+  p.mass = mass;
+  p.k_pages = pool->desc.k_pages;
+  p.page_base = d.page_base;
+  p.page_ids = d.page_ids;
+  p.seqs = t->d_seqs;
+  p.head_class = d.head_class;
+  p.num_seqs = t->num_seqs;
+  p.H = t->H;
+  p.Hkv = t->Hkv;
+  p.G = t->G;
+  p.T = rk::mass_tokens_per_step(t->G);
+  p.P = t->P;
+  p.log2P = log2i(t->P);
+  p.sink = t->sink;
+  p.window = t->window;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)pool->desc.head_dim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.total_q = (int32_t)total_q;
+  p.total_kv = (int32_t)total_kv;
+  const std::vector<rk::MassUnit> &units = t->mass_units[layer - t->layer_begin];
+  if (units.size() > (size_t)INT32_MAX) return fail(RK_ERR_UNSUPPORTED, "per-key mass: too many work units");
+  p.units = d.mass_units;
+  p.n_units = (int32_t)units.size();
+  hipError_t e = rk::launch_key_mass(p, pool->desc.head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "key mass kernel launch");
   return RK_OK;
   RK_GUARD_END
 }

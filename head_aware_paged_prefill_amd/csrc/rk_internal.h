@@ -25,6 +25,7 @@ struct SeqInfo {
   int32_t cu_q;           // first packed query row of the sequence
   int32_t n_q;            // kv_len - q_start
   int32_t q_start_local;  // first query position of the LOCAL heads (>= q_start)
+  int32_t kv_off;         // first key of the sequence in per-key outputs (sum of earlier kv_len)
 };
 
 struct Item {
@@ -113,7 +114,49 @@ struct KvWriteParams {
   int32_t rope_style;
 };
 
+// Per-key attention mass of one layer's call (bf16 pools, G <= 16).  A workgroup of 8 waves owns
+// mass_keys_per_unit(G) keys; its per-(head, key) LDS accumulators hold kMassAccFloats floats.  A step
+// stages kRowsPerItem query rows: mass_tokens_per_step(G) tokens (a multiple of 16, so that every
+// 16-row half of a 32-row MFMA block belongs to one head) of each of the G heads, the rest padding.
+constexpr int kMassAccFloats = 4096;
+constexpr int mass_keys_per_wave(int G) { return G <= 8 ? 64 : 32; }
+constexpr int mass_keys_per_unit(int G) { return 8 * mass_keys_per_wave(G); }
+constexpr int mass_tokens_per_step(int G) { return kRowsPerItem / G / 16 * 16; }
+struct MassUnit {
+  int32_t seq;  // < 0: padding
+  int32_t kv_head;
+  int32_t kblk;  // key block: keys kblk * mass_keys_per_unit(G) ..
+  int32_t qc;    // query chunk: steps qc * kMassChunkSteps .. of the head's token grid
+};
+struct MassParams {
+  const void *q;
+  const float *lse;     // [H][total_q], natural log
+  float *mass;          // [H][total_kv]
+  const void *k_pages;
+  const int32_t *page_base;
+  const int32_t *page_ids;
+  const SeqInfo *seqs;
+  const uint8_t *head_class;  // [Hkv] of the layer
+  int32_t num_seqs;
+  int32_t H;
+  int32_t Hkv;
+  int32_t G;
+  int32_t T;  // mass_tokens_per_step(G)
+  int32_t P;
+  int32_t log2P;
+  int32_t sink;
+  int32_t window;
+  float scale_log2;
+  int32_t total_q;
+  int32_t total_kv;
+  const MassUnit *units;  // launch order
+  int32_t n_units;
+};
+constexpr int kMassRun = 16;         // units placed together on one XCD
+constexpr int kMassChunkSteps = 64;  // steps per query chunk
+
 hipError_t launch_attention(const AttnParams &p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_key_mass(const MassParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_append(const KvWriteParams &p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_import(const KvWriteParams &p, int n_pages, int dtype, int head_dim, hipStream_t stream);
 

@@ -23,4 +23,14 @@ struct SchedInput {
 // Items (seq, kv head, first packed row, key tiles) in launch order; schedule padding has seq = -1.
 void schedule_layer(const SchedInput &in, std::vector<Item> &items);
 
+// Work units of the per-key mass pass: key block kblk (`keys` keys) of (seq, kv head) over query
+// chunk qc (kMassChunkSteps steps of `tokens` tokens on the token grid from the head's class start).
+// Only units with a visible pair are listed.  Runs of at most kMassRun units with the same (seq, kv
+// head, qc) -- key blocks reading the same query rows -- are placed on one XCD, each run on the XCD
+// with the fewest units so far: launch position i runs on XCD i % kXcd; padding has seq = -1.
+void mass_schedule(const SchedInput &in, int32_t keys, int32_t tokens, std::vector<MassUnit> &units);
+
+// An upper bound of mass_schedule's list length that holds for any head classes (head_class unused).
+int64_t mass_units_bound(const SchedInput &in, int32_t keys, int32_t tokens);
+
 }  // namespace rk

@@ -31,8 +31,9 @@ RK_ROPE_ROTATE_HALF, RK_ROPE_INTERLEAVED = 0, 1
 EXPORTS = [
     "rk_seg_pool_create", "rk_seg_pool_destroy", "rk_seg_pool_query", "rk_seg_pool_free_list",
     "rk_seg_tables_workspace_bytes", "rk_seg_build_tables", "rk_seg_tables_export", "rk_seg_tables_schedule",
-    "rk_seg_tables_stats", "rk_seg_tables_trim", "rk_seg_tables_destroy", "rk_seg_reuse_rerotate",
-    "rk_seg_append_kv", "rk_seg_attn_prefill", "rk_status_string", "rk_last_error", "rk_seg_version",
+    "rk_seg_tables_mass_schedule", "rk_seg_tables_stats", "rk_seg_tables_trim", "rk_seg_tables_destroy", "rk_seg_reuse_rerotate",
+    "rk_seg_append_kv", "rk_seg_attn_prefill", "rk_seg_key_mass", "rk_status_string", "rk_last_error",
+    "rk_seg_version",
 ]
 
 
@@ -84,12 +85,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rk_seg_build_tables": [VP, P(BatchDesc), VP, ctypes.c_size_t, VP, P(VP)],
         "rk_seg_tables_export": [VP, I32, I32, I32, P(I32), P(I32), I32, P(I32), P(I32), I32, P(I32)],
         "rk_seg_tables_schedule": [VP, I32, P(I32), I64, P(I64), P(I32), P(I32)],
+        "rk_seg_tables_mass_schedule": [VP, I32, P(I32), I64, P(I64), P(I32), P(I32), P(I32)],
         "rk_seg_tables_stats": [VP, P(TablesStats)],
         "rk_seg_tables_trim": [VP, VP],
         "rk_seg_tables_destroy": [VP, VP],
         "rk_seg_reuse_rerotate": [VP, VP, I32, I32, I32, I32, VP, VP, I64, I64, ctypes.c_double, I32, VP],
         "rk_seg_append_kv": [VP, VP, I32, VP, VP, VP],
         "rk_seg_attn_prefill": [VP, VP, I32, VP, VP, VP, VP, VP, ctypes.c_float, VP],
+        "rk_seg_key_mass": [VP, VP, I32, VP, VP, VP, ctypes.c_float, VP],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -275,6 +278,19 @@ def rk_seg_tables_schedule(tables: Tables, layer: int):
     return out[:n.value], T.value, BN.value
 
 
+def rk_seg_tables_mass_schedule(tables: Tables, layer: int):
+    """(units [n][4] = (seq, kv head, key block, query chunk), keys per unit, tokens per step, steps per
+    query chunk)."""
+    L = load()
+    n, K, T, S = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(L.rk_seg_tables_mass_schedule(tables.handle, layer, None, 0, ctypes.byref(n), ctypes.byref(K),
+                                         ctypes.byref(T), ctypes.byref(S)))
+    out = np.zeros((max(1, n.value), 4), np.int32)
+    _check(L.rk_seg_tables_mass_schedule(tables.handle, layer, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                         n.value, ctypes.byref(n), ctypes.byref(K), ctypes.byref(T), ctypes.byref(S)))
+    return out[:n.value], K.value, T.value, S.value
+
+
 def rk_seg_tables_stats(tables: Tables) -> dict:
     s = TablesStats()
     _check(load().rk_seg_tables_stats(tables.handle, ctypes.byref(s)))
@@ -320,6 +336,13 @@ def rk_seg_attn_prefill(tables: Tables, layer: int, q, k_new, v_new, o, lse=None
     """Append (unless k_new and v_new are None) and attend.  q, o: [total_q][H][D]; lse: [H][total_q] fp32."""
     _check(load().rk_seg_attn_prefill(tables.pool.handle, tables.handle, layer, _ptr(q), _ptr(k_new), _ptr(v_new),
                                       _ptr(o), _ptr(lse), float(softmax_scale), _stream(stream)))
+
+
+def rk_seg_key_mass(tables: Tables, layer: int, q, lse, mass, softmax_scale: float = 0.0, stream=None) -> None:
+    """Per-key attention mass.  q: [total_q][H][D] as given to rk_seg_attn_prefill; lse: the [H][total_q]
+    fp32 it returned; mass: [H][sum kv_len] fp32, written for every key."""
+    _check(load().rk_seg_key_mass(tables.pool.handle, tables.handle, layer, _ptr(q), _ptr(lse), _ptr(mass),
+                                  float(softmax_scale), _stream(stream)))
 
 
 def rk_seg_version() -> str:

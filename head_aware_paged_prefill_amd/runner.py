@@ -72,6 +72,15 @@ class PrefillRunner:
         rk_seg.rk_seg_attn_prefill(self.tables, layer, q, k_new, v_new, o, lse, scale, stream)
         return o, lse
 
+    def key_mass(self, q, lse, mass=None, layer: Optional[int] = None, scale: float = 0.0, stream=None):
+        """Per-key attention mass [H][sum kv_len] fp32 of the call attended last (same q, its lse)."""
+        wl = self.wl
+        layer = wl.layer if layer is None else layer
+        if mass is None:
+            mass = torch.empty((wl.num_q_heads, sum(wl.kv_lens)), dtype=torch.float32, device=self.device)
+        rk_seg.rk_seg_key_mass(self.tables, layer, q, lse, mass, scale, stream)
+        return mass
+
     def release(self, trim: bool = True):
         if self.tables is not None:
             if trim:

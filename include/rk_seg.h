@@ -191,6 +191,18 @@ rk_status rk_seg_tables_export(const rk_tables *tables, int32_t layer, int32_t k
 rk_status rk_seg_tables_schedule(const rk_tables *tables, int32_t layer, int32_t *items, int64_t cap,
                                  int64_t *n_items, int32_t *tokens_per_item, int32_t *key_tile);
 
+/* Export the per-key mass work units of one layer (rk_seg_key_mass) in launch order: units [cap][4] =
+ * (seq, kv_head, key block, query chunk).  Key block k holds keys [k * keys_per_unit, ...) of the
+ * sequence; query chunk c holds the query tokens start + [c * steps_per_chunk * tokens_per_step,
+ * (c + 1) * steps_per_chunk * tokens_per_step) of the head, where start is the head's first query
+ * position.  Exactly the (seq, kv_head, key block, query chunk) with at least one visible (query,
+ * key) pair appear, each once.  Workgroup i runs on XCD i % 8; entries with seq = -1 are empty
+ * slots.  The list is empty when the group size num_q_heads / num_kv_heads exceeds 16 (the mass
+ * pass does not support it).  Any output pointer may be NULL. */
+rk_status rk_seg_tables_mass_schedule(const rk_tables *tables, int32_t layer, int32_t *units, int64_t cap,
+                                      int64_t *n_units, int32_t *keys_per_unit, int32_t *tokens_per_step,
+                                      int32_t *steps_per_chunk);
+
 rk_status rk_seg_tables_stats(const rk_tables *tables, rk_tables_stats *out);
 
 /* After the call: LOCAL heads keep their sink pages and the pages covering
@@ -237,6 +249,23 @@ rk_status rk_seg_append_kv(rk_pool *pool, const rk_tables *tables, int32_t layer
 rk_status rk_seg_attn_prefill(rk_pool *pool, const rk_tables *tables, int32_t layer, const void *q,
                               const void *k_new, const void *v_new, void *o, float *lse,
                               float softmax_scale, void *stream);
+
+/* Per-key attention mass of one layer's call: the routing signal of the sparse FFN, whose dense
+ * FFN runs only on the top-k tokens by attention score (page "小红书把 KV Cache 按「头」拆了…",
+ * section 事件内容, item 2; page "RedKnot – 小红书研发并开源的长上下文大模型推理引擎", section
+ * RedKnot技术原理, 3).  For every q head h and key j < kv_len[b] of sequence b:
+ *   mass[h][kv_off(b) + j] = sum over the call's queries i of head h (from its class start) of
+ *                            exp(scale * q_i.k_j - lse[h][i]) over the visible pairs (i, j),
+ * with kv_off(b) = kv_len[0] + ... + kv_len[b-1]; keys no query sees get 0.  Every such entry is
+ * written.  q: as given to rk_seg_attn_prefill; lse: [num_q_heads][total_q] fp32, the lse that
+ * rk_seg_attn_prefill returned for that q (natural log); mass: device fp32
+ * [num_q_heads][sum kv_len], 4-byte aligned.  softmax_scale as for rk_seg_attn_prefill.  The K
+ * pages must hold what attention read (run it after rk_seg_attn_prefill, before the tables are
+ * trimmed or destroyed).  Requires a bf16 pool and num_q_heads / num_kv_heads <= 16.
+ * Errors: RK_ERR_INVALID_ARG, RK_ERR_STATE, RK_ERR_UNSUPPORTED (fp32 pool, more than 16 q heads per
+ * KV head, more than 2^31 keys), RK_ERR_HIP. */
+rk_status rk_seg_key_mass(rk_pool *pool, const rk_tables *tables, int32_t layer, const void *q,
+                          const float *lse, float *mass, float softmax_scale, void *stream);
 
 /* -- diagnostics --------------------------------------------------------------------------- */
 
