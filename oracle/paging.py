@@ -18,7 +18,10 @@ Readings where the pages are silent:
     its head in ascending (layer, kv head, seq, logical page) order (LIFO reuse);
     a build that does not fit takes nothing (transactional);
   * trimming after the call keeps, for LOCAL heads, the sink pages and the pages
-    covering [max(0, kv_len - W + 1), kv_len) -- what the next query would see.
+    covering [max(0, kv_len - W + 1), kv_len) -- what the next query would see;
+  * the next call on the same sequences (decode) keeps every still-held page in
+    place, frees the others first and then allocates the missing ones, both in the
+    (layer, kv head, seq, logical page) order.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 """
@@ -134,6 +137,30 @@ class PoolReplay:
             freed.extend(t[p] for p in sorted(t) if p not in keep)
         self._push(freed)
         return out
+
+    def advance(self, tables: Dict, head_class: np.ndarray, kv_lens: Sequence[int], n_new: Sequence[int], sink: int,
+                window: int, page_size: int):
+        """The next call on the same sequences (decode, or a further chunk): sequence b gains n_new[b]
+        tokens, which are its queries, so q_start becomes the old kv_len.  Each (layer, kv head, seq)
+        then holds held_pages(class, old kv_len, new kv_len); a logical page it held before keeps its
+        physical page (and contents), the pages it no longer holds are freed first, the missing ones
+        allocated after, both in ascending (layer, kv head, seq, logical page) order.  Transactional.
+        Returns (tables, new kv_lens)."""
+        new_kv = [int(L) + int(n) for L, n in zip(kv_lens, n_new)]
+        plan = {}
+        for key in sorted(tables):
+            l, g, b = key
+            plan[key] = held_pages(int(head_class[l, g]), int(kv_lens[b]), new_kv[b], sink, window, page_size)
+        freed = [tables[key][p] for key in sorted(tables) for p in sorted(tables[key]) if p not in set(plan[key])]
+        fresh = [(key, p) for key in sorted(plan) for p in plan[key] if p not in tables[key]]
+        if len(fresh) > len(self.free) + len(freed):
+            raise OutOfPages(len(fresh))
+        self._push(freed)
+        out = {key: {p: tables[key][p] for p in plan[key] if p in tables[key]} for key in plan}
+        for key, p in fresh:
+            out[key][p] = self.free.popleft()
+        out = {key: dict(sorted(t.items())) for key, t in out.items()}
+        return out, new_kv
 
     def release(self, tables: Dict) -> None:
         freed = []

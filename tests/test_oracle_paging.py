@@ -139,3 +139,59 @@ def test_held_token_ranges_are_the_runs_of_the_visible_union():
         for cls in (GLOBAL, LOCAL):
             m = attention.visibility_mask(cls, np.arange(qs, L), L, S, W)
             assert paging.held_token_ranges(cls, qs, L, S, W) == paging.visible_intervals(m.any(axis=0))
+
+
+def _golden_tables(d):
+    return {tuple(int(x) for x in k.split(",")): {int(p): v for p, v in t.items()} for k, t in d.items()}
+
+
+def test_golden_advance_replay():
+    # hand-derived: pages that stay held keep their ids, released pages are pushed first, new pages
+    # are taken from the head after, both in (layer, kv head, seq, logical page) order
+    g = json.load(open(os.path.join(GOLDEN, "advance_small.json")))
+    hc = np.array(g["head_class"], np.uint8)
+    pool = paging.PoolReplay(g["num_pages"])
+    t = pool.build(0, 1, hc, g["build"]["q_starts"], g["build"]["kv_lens"], g["sink"], g["window"], g["page_size"])
+    assert t == _golden_tables(g["tables_after_build"])
+    kv = g["build"]["kv_lens"]
+    t = pool.trim(t, hc, kv, g["sink"], g["window"], g["page_size"])
+    for st in g["steps"]:
+        t, kv = pool.advance(t, hc, kv, st["n_new"], g["sink"], g["window"], g["page_size"])
+        assert kv == st["kv_lens"]
+        assert t == _golden_tables(st["tables"])
+        assert list(pool.free) == st["free"]
+    before = (dict(t), list(pool.free))
+    with pytest.raises(paging.OutOfPages):
+        pool.advance(t, hc, kv, g["out_of_pages"]["n_new"], g["sink"], g["window"], g["page_size"])
+    assert (dict(t), list(pool.free)) == before
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_advance_holds_exactly_the_pages_of_the_visible_keys(seed):
+    # after any sequence of advances, a (kv head, seq) holds the pages of the keys some query of the
+    # latest call sees (brute force over the dense mask), and no id is held twice
+    rng = np.random.Generator(np.random.PCG64(3100 + seed))
+    Hkv, P = 3, int(rng.choice([4, 8, 16]))
+    S, W = int(rng.choice([0, 1, 5])), int(rng.choice([1, 3, 17, 40]))
+    hc = rng.integers(0, 2, size=(1, Hkv)).astype(np.uint8)
+    kv = [int(x) for x in rng.integers(1, 60, size=2)]
+    qs = [int(rng.integers(0, L)) for L in kv]
+    pool = paging.PoolReplay(4000)
+    t = pool.build(0, 1, hc, qs, kv, S, W, P)
+    for _ in range(6):
+        n_new = [int(x) for x in rng.integers(0, 9, size=2)]
+        old = kv
+        t, kv = pool.advance(t, hc, kv, n_new, S, W, P)
+        ids = [pid for tt in t.values() for pid in tt.values()]
+        assert len(ids) == len(set(ids)) and len(ids) + len(pool.free) == 4000
+        for (l, g, b), tt in t.items():
+            if kv[b] == 0:
+                assert tt == {}
+                continue
+            pos = np.arange(old[b], kv[b])
+            m = attention.visibility_mask(int(hc[0, g]), pos, kv[b], S, W) if len(pos) else np.zeros((0, kv[b]), bool)
+            want = sorted(set((np.flatnonzero(m.any(axis=0)) // P).tolist()))
+            if not len(pos):  # no query: the retained state, what a query at kv_len would see
+                m = attention.visibility_mask(int(hc[0, g]), np.array([kv[b]]), kv[b] + 1, S, W)[:, :kv[b]]
+                want = sorted(set((np.flatnonzero(m[0]) // P).tolist()))
+            assert sorted(tt) == want
