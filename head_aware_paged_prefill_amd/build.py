@@ -36,7 +36,7 @@ def _run(cmd, verbose):
 
 
 HOST_SOURCES = ["rk_host.cpp", "rk_sched.cpp"]
-HIP_SOURCES = ["rk_attn.hip", "rk_kernels.hip", "rk_mass.hip"]
+HIP_SOURCES = ["rk_attn.hip", "rk_kernels.hip", "rk_mass.hip", "rk_decode.hip"]
 
 
 def build(verbose: bool = False, out: str = LIB, extra_hip: list | None = None) -> str:

@@ -143,6 +143,9 @@ struct rk_tables {
   std::vector<std::vector<rk::Item>> items;     // per layer of the call, in launch order
   std::vector<std::vector<int32_t>> app_items;  // per layer: (seq, logical page) pairs
   std::vector<std::vector<rk::MassUnit>> mass_units;  // per layer: per-key mass work units, launch order
+  bool decode_shaped = false;                          // every sequence has at most one query row
+  std::vector<std::vector<rk::DecItem>> dec_items;     // per layer: split-KV decode items, slot order
+  std::vector<std::vector<int32_t>> dec_comb;          // per layer: first item of (seq, kv head)
   // device view
   void *d_ws = nullptr;
   size_t ws_used = 0;
@@ -153,9 +156,12 @@ struct rk_tables {
     const rk::Item *items;
     const int32_t *app;
     const rk::MassUnit *mass_units;
+    const rk::DecItem *dec_items;
+    const int32_t *dec_comb;
   };
   std::vector<LayerDev> dev;
   const rk::SeqInfo *d_seqs = nullptr;
+  float *d_part_o = nullptr, *d_part_lse = nullptr;  // decode partials, shared by the layers
   StagingBuf staging;
   hipEvent_t ev = nullptr;
   bool trimmed = false;
@@ -173,8 +179,17 @@ namespace {
 // Device workspace layout of one build.  Offsets are relative to the workspace base.
 struct WsLayout {
   size_t seqs = 0;
-  std::vector<size_t> page_base, page_ids, head_class, items, app, mass;
+  std::vector<size_t> page_base, page_ids, head_class, items, app, mass, dec_items, dec_comb;
+  size_t part_o = 0, part_lse = 0;  // decode-shaped calls only
   size_t total = 0;
+};
+
+// Host schedules computed while sizing the workspace.
+struct CallSched {
+  std::vector<std::vector<rk::MassUnit>> mass;
+  bool decode = false;
+  std::vector<std::vector<rk::DecItem>> dec;
+  std::vector<std::vector<int32_t>> comb;
 };
 
 // first packed position of sequence b: the GLOBAL heads' start
@@ -214,26 +229,39 @@ rk_status check_batch(const rk_pool *pool, const rk_batch_desc *bd) {
   return RK_OK;
 }
 
-// The per-key mass units of each layer are scheduled here (their count sizes the workspace) and
-// returned in *mass_units when it is not null.
-WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, std::vector<std::vector<rk::MassUnit>> *mass_units) {
+// The per-key mass units and the decode items of each layer are scheduled here (their counts size the
+// workspace, through bounds that do not depend on the head classes, so that one workspace serves
+// every layer of a model) and returned in *sched when it is not null.
+WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, CallSched *sched) {
   const rk_pool_desc &pd = pool->desc;
   WsLayout w;
   std::vector<int32_t> q_begin(std::max(1, bd->num_seqs));
-  for (int32_t b = 0; b < bd->num_seqs; ++b) q_begin[b] = batch_q_begin(bd, b);
-  if (mass_units) mass_units->assign(bd->layer_end - bd->layer_begin, {});
+  bool decode = true;  // every sequence has at most one query row
+  for (int32_t b = 0; b < bd->num_seqs; ++b) {
+    q_begin[b] = batch_q_begin(bd, b);
+    decode = decode && bd->kv_len[b] - q_begin[b] <= 1;
+  }
+  const int32_t nl = bd->layer_end - bd->layer_begin;
+  const int32_t G = bd->num_q_heads / pd.num_kv_heads;
+  const int32_t T = rk::kRowsPerItem / G;
+  decode = decode && G <= 16;
+  if (sched) {
+    sched->mass.assign(nl, {});
+    sched->decode = decode;
+    sched->dec.assign(decode ? nl : 0, {});
+    sched->comb.assign(decode ? nl : 0, {});
+  }
   size_t off = 0;
   w.seqs = off;
   off = align_up(off + sizeof(rk::SeqInfo) * std::max(1, bd->num_seqs));
-  int32_t G = bd->num_q_heads / pd.num_kv_heads;
-  int32_t T = rk::kRowsPerItem / G;
   int64_t n_logical = 0, n_items = 0, n_app = 0;
   for (int32_t b = 0; b < bd->num_seqs; ++b) {
-    int32_t L = bd->kv_len[b], qs = batch_q_begin(bd, b);
+    int32_t L = bd->kv_len[b], qs = q_begin[b];
     n_logical += ceil_div(L, pd.page_size);
     n_items += ceil_div(L - qs, T);
     if (L > qs) n_app += (L - 1) / pd.page_size - qs / pd.page_size + 1;
   }
+  int64_t dec_bound = 0;
   for (int32_t l = bd->layer_begin; l < bd->layer_end; ++l) {
     w.page_base.push_back(off);
     off = align_up(off + sizeof(int32_t) * std::max<int64_t>(1, (int64_t)pd.num_kv_heads * bd->num_seqs));
@@ -248,12 +276,24 @@ WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, std::vector<std::
     off = align_up(off + 2 * sizeof(int32_t) * std::max<int64_t>(1, n_app));
     rk::SchedInput si{bd->num_seqs, pd.num_kv_heads, T, pd.head_dim, pd.dtype == RK_F32 ? 4 : 2, bd->sink, bd->window,
                       &bd->head_class[(size_t)l * pd.num_kv_heads], bd->kv_len, bd->q_start, q_begin.data()};
-    // sized by a bound that does not depend on the head classes, so that one workspace serves
-    // every layer of a model
     const int32_t mk = rk::mass_keys_per_unit(G), mt = rk::mass_tokens_per_step(G);
-    if (mass_units && G <= 16) rk::mass_schedule(si, mk, mt, (*mass_units)[l - bd->layer_begin]);
+    if (sched && G <= 16) rk::mass_schedule(si, mk, mt, sched->mass[l - bd->layer_begin]);
     w.mass.push_back(off);
     off = align_up(off + sizeof(rk::MassUnit) * std::max<int64_t>(1, G <= 16 ? rk::mass_units_bound(si, mk, mt) : 0));
+    if (decode) {
+      if (sched) rk::decode_schedule(si, sched->dec[l - bd->layer_begin], sched->comb[l - bd->layer_begin]);
+      dec_bound = rk::decode_items_bound(si);
+      w.dec_items.push_back(off);
+      off = align_up(off + sizeof(rk::DecItem) * dec_bound);
+      w.dec_comb.push_back(off);
+      off = align_up(off + sizeof(int32_t) * ((int64_t)bd->num_seqs * pd.num_kv_heads + 1));
+    }
+  }
+  if (decode) {
+    w.part_o = off;
+    off = align_up(off + sizeof(float) * dec_bound * G * pd.head_dim);
+    w.part_lse = off;
+    off = align_up(off + sizeof(float) * dec_bound * G);
   }
   w.total = off;
   return w;
@@ -298,14 +338,15 @@ rk_status release_device(rk_tables *t) {
   return st;
 }
 
-rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, size_t ws_bytes, void *stream,
-                            rk_tables **out) {
-  if (!out) return fail(RK_ERR_INVALID_ARG, "null out");
+// Everything of a call but its physical pages and device view: shape, held logical pages, schedules
+// and counters.  No side effects on the pool.
+rk_status prepare_tables(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, size_t ws_bytes, WsLayout &ws,
+                         std::unique_ptr<rk_tables> &out) {
   rk_status st = check_batch(pool, bd);
   if (st != RK_OK) return st;
   const rk_pool_desc &pd = pool->desc;
-  std::vector<std::vector<rk::MassUnit>> mass_units;
-  WsLayout ws = plan_ws(pool, bd, &mass_units);
+  CallSched sched;
+  ws = plan_ws(pool, bd, &sched);
   if (d_ws) {
     if ((reinterpret_cast<uintptr_t>(d_ws) & (kAlign - 1)) != 0)
       return fail(RK_ERR_INVALID_ARG, "workspace not 256-byte aligned");
@@ -315,7 +356,10 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
 
   std::unique_ptr<rk_tables> t(new rk_tables());
   t->pool = pool;
-  t->mass_units = std::move(mass_units);
+  t->mass_units = std::move(sched.mass);
+  t->decode_shaped = sched.decode;
+  t->dec_items = std::move(sched.dec);
+  t->dec_comb = std::move(sched.comb);
   t->layer_begin = bd->layer_begin;
   t->layer_end = bd->layer_end;
   t->num_seqs = bd->num_seqs;
@@ -353,18 +397,15 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
         t->held_off[k + 1] = t->held_off[k] + n;
       }
   const int64_t need = t->held_off[nkeys];
-  if (need > (int64_t)pool->free_stack.size())
-    return fail(RK_ERR_OUT_OF_PAGES, "call holds %lld pages, %zu free", (long long)need, pool->free_stack.size());
-
   t->held_logical.resize(need);
-  t->held_phys.resize(need);
+  t->held_phys.assign(need, -1);
   for (int64_t k = 0; k < nkeys; ++k) {
     int64_t o = t->held_off[k];
     for (int r = 0; r < nrun[k]; ++r)
       for (int32_t p = runs[2 * k + r].p0; p < runs[2 * k + r].p1; ++p) t->held_logical[o++] = p;
   }
 
-  // schedules (host only, no side effects yet)
+  // schedules
   t->items.resize(nl);
   t->app_items.resize(nl);
   int64_t key_tiles = 0, n_items = 0;
@@ -387,7 +428,7 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
     }
   }
 
-  // stats
+  // counters
   rk_tables_stats &s = t->stats;
   s.pages_held = need;
   s.total_q = t->cu_q[t->num_seqs];
@@ -403,80 +444,199 @@ rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, 
         if (cls == RK_GLOBAL) s.visible_pairs_global += v;
       }
     }
+  out = std::move(t);
+  return RK_OK;
+}
 
-  // device staging (before touching the pool, so that a failure leaves it unchanged)
-  if (d_ws) {
-    hipError_t e;
-    t->staging = take_staging(pool, ws.total, &e);
-    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (table staging)");
-    e = hipEventCreateWithFlags(&t->ev, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      pool->staging_cache.push_back(t->staging);
-      t->staging = StagingBuf{};
-      t->ev = nullptr;
-      return hip_fail(e, "hipEventCreate");
-    }
+// Pinned staging and the upload event of t's device view (before the pool is touched, so that a
+// failure leaves it unchanged).
+rk_status acquire_staging(rk_pool *pool, rk_tables *t, const WsLayout &ws) {
+  hipError_t e;
+  t->staging = take_staging(pool, ws.total, &e);
+  if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (table staging)");
+  e = hipEventCreateWithFlags(&t->ev, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    pool->staging_cache.push_back(t->staging);
+    t->staging = StagingBuf{};
+    t->ev = nullptr;
+    return hip_fail(e, "hipEventCreate");
   }
+  return RK_OK;
+}
 
+// Writes t's device view (pages assigned) into its staging and uploads it into d_ws on the stream.
+hipError_t fill_and_upload(rk_tables *t, const WsLayout &ws, void *d_ws, void *stream) {
+  char *h = static_cast<char *>(t->staging.ptr);
+  std::memset(h, 0, ws.total);
+  rk::SeqInfo *seqs = reinterpret_cast<rk::SeqInfo *>(h + ws.seqs);
+  int64_t kv_off = 0;  // per-key outputs need it below 2^31 (checked where they are computed)
+  for (int32_t b = 0; b < t->num_seqs; ++b) {
+    seqs[b] = {t->q_begin[b], t->kv_len[b], t->cu_q[b], t->kv_len[b] - t->q_begin[b], t->q_start[b],
+               (int32_t)std::min<int64_t>(kv_off, INT32_MAX)};
+    kv_off += t->kv_len[b];
+  }
+  char *dbase = static_cast<char *>(d_ws);
+  t->d_seqs = reinterpret_cast<const rk::SeqInfo *>(dbase + ws.seqs);
+  const int32_t nl = t->layer_end - t->layer_begin;
+  t->dev.resize(nl);
+  for (int32_t l = t->layer_begin; l < t->layer_end; ++l) {
+    const int32_t li = l - t->layer_begin;
+    int32_t *pbase = reinterpret_cast<int32_t *>(h + ws.page_base[li]);
+    int32_t *pids = reinterpret_cast<int32_t *>(h + ws.page_ids[li]);
+    int32_t off = 0;
+    for (int32_t g = 0; g < t->Hkv; ++g)
+      for (int32_t b = 0; b < t->num_seqs; ++b) {
+        pbase[g * t->num_seqs + b] = off;
+        int32_t nlog = t->n_logical(b);
+        std::fill(pids + off, pids + off + nlog, -1);
+        int64_t k = t->key(l, g, b);
+        for (int64_t i = t->held_off[k]; i < t->held_off[k + 1]; ++i) pids[off + t->held_logical[i]] = t->held_phys[i];
+        off += nlog;
+      }
+    std::memcpy(h + ws.head_class[li], &t->head_class[(size_t)l * t->Hkv], t->Hkv);
+    std::memcpy(h + ws.items[li], t->items[li].data(), sizeof(rk::Item) * t->items[li].size());
+    std::memcpy(h + ws.app[li], t->app_items[li].data(), sizeof(int32_t) * t->app_items[li].size());
+    std::memcpy(h + ws.mass[li], t->mass_units[li].data(), sizeof(rk::MassUnit) * t->mass_units[li].size());
+    const rk::DecItem *dec_items = nullptr;
+    const int32_t *dec_comb = nullptr;
+    if (t->decode_shaped) {
+      std::memcpy(h + ws.dec_items[li], t->dec_items[li].data(), sizeof(rk::DecItem) * t->dec_items[li].size());
+      std::memcpy(h + ws.dec_comb[li], t->dec_comb[li].data(), sizeof(int32_t) * t->dec_comb[li].size());
+      dec_items = reinterpret_cast<const rk::DecItem *>(dbase + ws.dec_items[li]);
+      dec_comb = reinterpret_cast<const int32_t *>(dbase + ws.dec_comb[li]);
+    }
+    t->dev[li] = {reinterpret_cast<const int32_t *>(dbase + ws.page_base[li]),
+                  reinterpret_cast<const int32_t *>(dbase + ws.page_ids[li]),
+                  reinterpret_cast<const uint8_t *>(dbase + ws.head_class[li]),
+                  reinterpret_cast<const rk::Item *>(dbase + ws.items[li]),
+                  reinterpret_cast<const int32_t *>(dbase + ws.app[li]),
+                  reinterpret_cast<const rk::MassUnit *>(dbase + ws.mass[li]),
+                  dec_items,
+                  dec_comb};
+  }
+  t->d_part_o = t->decode_shaped ? reinterpret_cast<float *>(dbase + ws.part_o) : nullptr;
+  t->d_part_lse = t->decode_shaped ? reinterpret_cast<float *>(dbase + ws.part_lse) : nullptr;
+  hipStream_t sm = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(d_ws, h, ws.total, hipMemcpyHostToDevice, sm);
+  if (e == hipSuccess) e = hipEventRecord(t->ev, sm);
+  if (e == hipSuccess) {
+    t->d_ws = d_ws;
+    t->ws_used = ws.total;
+  }
+  return e;
+}
+
+rk_status build_tables_impl(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, size_t ws_bytes, void *stream,
+                            rk_tables **out) {
+  if (!out) return fail(RK_ERR_INVALID_ARG, "null out");
+  WsLayout ws;
+  std::unique_ptr<rk_tables> t;
+  rk_status st = prepare_tables(pool, bd, d_ws, ws_bytes, ws, t);
+  if (st != RK_OK) return st;
+  const int64_t need = (int64_t)t->held_phys.size();
+  if (need > (int64_t)pool->free_stack.size())
+    return fail(RK_ERR_OUT_OF_PAGES, "call holds %lld pages, %zu free", (long long)need, pool->free_stack.size());
+  if (d_ws) {
+    st = acquire_staging(pool, t.get(), ws);
+    if (st != RK_OK) return st;
+  }
   // allocate: pop from the head of the free list in (layer, kv head, seq, logical page) order
   for (int64_t i = 0; i < need; ++i) {
     t->held_phys[i] = pool->free_stack.back();
     pool->free_stack.pop_back();
   }
-
   if (d_ws) {
-    char *h = static_cast<char *>(t->staging.ptr);
-    std::memset(h, 0, ws.total);
-    rk::SeqInfo *seqs = reinterpret_cast<rk::SeqInfo *>(h + ws.seqs);
-    int64_t kv_off = 0;  // per-key outputs need it below 2^31 (checked where they are computed)
-    for (int32_t b = 0; b < t->num_seqs; ++b) {
-      seqs[b] = {t->q_begin[b], t->kv_len[b], t->cu_q[b], t->kv_len[b] - t->q_begin[b], t->q_start[b],
-                 (int32_t)std::min<int64_t>(kv_off, INT32_MAX)};
-      kv_off += t->kv_len[b];
-    }
-    char *dbase = static_cast<char *>(d_ws);
-    t->d_seqs = reinterpret_cast<const rk::SeqInfo *>(dbase + ws.seqs);
-    t->dev.resize(nl);
-    for (int32_t l = bd->layer_begin; l < bd->layer_end; ++l) {
-      const int32_t li = l - bd->layer_begin;
-      int32_t *pbase = reinterpret_cast<int32_t *>(h + ws.page_base[li]);
-      int32_t *pids = reinterpret_cast<int32_t *>(h + ws.page_ids[li]);
-      int32_t off = 0;
-      for (int32_t g = 0; g < t->Hkv; ++g)
-        for (int32_t b = 0; b < t->num_seqs; ++b) {
-          pbase[g * t->num_seqs + b] = off;
-          int32_t nlog = t->n_logical(b);
-          std::fill(pids + off, pids + off + nlog, -1);
-          int64_t k = t->key(l, g, b);
-          for (int64_t i = t->held_off[k]; i < t->held_off[k + 1]; ++i) pids[off + t->held_logical[i]] = t->held_phys[i];
-          off += nlog;
-        }
-      std::memcpy(h + ws.head_class[li], &t->head_class[(size_t)l * t->Hkv], t->Hkv);
-      std::memcpy(h + ws.items[li], t->items[li].data(), sizeof(rk::Item) * t->items[li].size());
-      std::memcpy(h + ws.app[li], t->app_items[li].data(), sizeof(int32_t) * t->app_items[li].size());
-      std::memcpy(h + ws.mass[li], t->mass_units[li].data(), sizeof(rk::MassUnit) * t->mass_units[li].size());
-      t->dev[li] = {reinterpret_cast<const int32_t *>(dbase + ws.page_base[li]),
-                    reinterpret_cast<const int32_t *>(dbase + ws.page_ids[li]),
-                    reinterpret_cast<const uint8_t *>(dbase + ws.head_class[li]),
-                    reinterpret_cast<const rk::Item *>(dbase + ws.items[li]),
-                    reinterpret_cast<const int32_t *>(dbase + ws.app[li]),
-                    reinterpret_cast<const rk::MassUnit *>(dbase + ws.mass[li])};
-    }
-    hipStream_t sm = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(d_ws, h, ws.total, hipMemcpyHostToDevice, sm);
-    if (e == hipSuccess) e = hipEventRecord(t->ev, sm);
+    hipError_t e = fill_and_upload(t.get(), ws, d_ws, stream);
     if (e != hipSuccess) {
       // undo the allocation so that the pool is unchanged
       for (int64_t i = need - 1; i >= 0; --i) pool->free_stack.push_back(t->held_phys[i]);
-      hipStreamSynchronize(sm);
+      hipStreamSynchronize(static_cast<hipStream_t>(stream));
       release_device(t.get());
       return hip_fail(e, "table upload");
     }
-    t->d_ws = d_ws;
-    t->ws_used = ws.total;
   }
   pool->live_tables++;
   *out = t.release();
+  return RK_OK;
+}
+
+// The call after t's on the same sequences: sequence b gains n_new[b] tokens, which are its queries
+// (q_start = q_start_global = the old kv_len).  Pages that stay held keep their physical page and
+// contents; pages no longer held are freed first (in (layer, kv head, seq, logical page) order),
+// then the new pages are taken from the head of the free list in the same order.
+rk_status advance_desc(const rk_tables *t, const int32_t *n_new, std::vector<int32_t> &qs, std::vector<int32_t> &kv,
+                       rk_batch_desc &nb) {
+  if (t->num_seqs > 0 && !n_new) return fail(RK_ERR_INVALID_ARG, "null n_new");
+  qs.resize(std::max(1, t->num_seqs));
+  kv.resize(std::max(1, t->num_seqs));
+  for (int32_t b = 0; b < t->num_seqs; ++b) {
+    if (n_new[b] < 0 || (int64_t)t->kv_len[b] + n_new[b] > INT32_MAX)
+      return fail(RK_ERR_INVALID_ARG, "seq %d: n_new %d out of range", b, n_new[b]);
+    qs[b] = t->kv_len[b];
+    kv[b] = t->kv_len[b] + n_new[b];
+  }
+  nb = rk_batch_desc{};
+  nb.layer_begin = t->layer_begin;
+  nb.layer_end = t->layer_end;
+  nb.num_seqs = t->num_seqs;
+  nb.num_q_heads = t->H;
+  nb.q_start = qs.data();
+  nb.kv_len = kv.data();
+  nb.head_class = t->head_class.data();
+  nb.sink = t->sink;
+  nb.window = t->window;
+  nb.q_start_global = nullptr;
+  return RK_OK;
+}
+
+rk_status advance_impl(rk_pool *pool, rk_tables *t, const int32_t *n_new, void *d_ws, size_t ws_bytes, void *stream) {
+  std::vector<int32_t> qs, kv;
+  rk_batch_desc nb;
+  rk_status st = advance_desc(t, n_new, qs, kv, nb);
+  if (st != RK_OK) return st;
+  WsLayout ws;
+  std::unique_ptr<rk_tables> nt;
+  st = prepare_tables(pool, &nb, d_ws, ws_bytes, ws, nt);
+  if (st != RK_OK) return st;
+  // pages per key: kept (same logical page), freed (old only), new (new only)
+  std::vector<int32_t> freed;
+  std::vector<int64_t> fresh;  // indices into nt->held_phys
+  const int64_t nkeys = (int64_t)t->held_off.size() - 1;
+  for (int64_t k = 0; k < nkeys; ++k) {
+    int64_t i = t->held_off[k], i1 = t->held_off[k + 1];
+    int64_t j = nt->held_off[k], j1 = nt->held_off[k + 1];
+    while (i < i1 || j < j1) {
+      if (j == j1 || (i < i1 && t->held_logical[i] < nt->held_logical[j])) {
+        freed.push_back(t->held_phys[i++]);
+      } else if (i == i1 || nt->held_logical[j] < t->held_logical[i]) {
+        fresh.push_back(j++);
+      } else {
+        nt->held_phys[j++] = t->held_phys[i++];
+      }
+    }
+  }
+  if ((int64_t)fresh.size() > (int64_t)(pool->free_stack.size() + freed.size()))
+    return fail(RK_ERR_OUT_OF_PAGES, "advance needs %zu new pages, %zu free after releasing %zu", fresh.size(),
+                pool->free_stack.size() + freed.size(), freed.size());
+  st = release_device(t);  // the previous upload has landed; its staging goes back to the pool
+  if (st != RK_OK) return st;
+  if (d_ws) {
+    st = acquire_staging(pool, nt.get(), ws);
+    if (st != RK_OK) return st;
+  }
+  // from here on the pool changes
+  push_free(pool, freed);
+  for (int64_t j : fresh) {
+    nt->held_phys[j] = pool->free_stack.back();
+    pool->free_stack.pop_back();
+  }
+  hipError_t e = hipSuccess;
+  if (d_ws) e = fill_and_upload(nt.get(), ws, d_ws, stream);
+  // t becomes the new call (same handle); its old staging and event were released above
+  nt->pool = pool;
+  if (!d_ws || e != hipSuccess) nt->d_ws = nullptr;
+  *t = std::move(*nt);
+  if (e != hipSuccess) return hip_fail(e, "table upload (the tables keep their pages, without a device view)");
   return RK_OK;
 }
 
@@ -633,6 +793,29 @@ rk_status rk_seg_build_tables(rk_pool *pool, const rk_batch_desc *batch, void *d
   RK_GUARD_END
 }
 
+rk_status rk_seg_tables_advance_workspace_bytes(const rk_pool *pool, const rk_tables *t, const int32_t *n_new,
+                                                size_t *bytes) {
+  RK_GUARD_BEGIN
+  if (!pool || !t || t->pool != pool || !bytes) return fail(RK_ERR_INVALID_ARG, "null or foreign argument");
+  std::vector<int32_t> qs, kv;
+  rk_batch_desc nb;
+  rk_status st = advance_desc(t, n_new, qs, kv, nb);
+  if (st != RK_OK) return st;
+  st = check_batch(pool, &nb);
+  if (st != RK_OK) return st;
+  *bytes = plan_ws(pool, &nb, nullptr).total;
+  return RK_OK;
+  RK_GUARD_END
+}
+
+rk_status rk_seg_tables_advance(rk_pool *pool, rk_tables *t, const int32_t *n_new, void *d_workspace, size_t ws_bytes,
+                                void *stream) {
+  RK_GUARD_BEGIN
+  if (!pool || !t || t->pool != pool) return fail(RK_ERR_INVALID_ARG, "null or foreign tables");
+  return advance_impl(pool, t, n_new, d_workspace, ws_bytes, stream);
+  RK_GUARD_END
+}
+
 rk_status rk_seg_tables_export(const rk_tables *t, int32_t layer, int32_t kv_head, int32_t seq, int32_t *seg_tok_begin,
                                int32_t *seg_npages, int32_t seg_cap, int32_t *n_segs, int32_t *page_ids,
                                int32_t page_cap, int32_t *n_pages) {
@@ -695,6 +878,29 @@ rk_status rk_seg_tables_mass_schedule(const rk_tables *t, int32_t layer, int32_t
       units[4 * i + 2] = v[i].kblk;
       units[4 * i + 3] = v[i].qc;
     }
+  return RK_OK;
+}
+
+rk_status rk_seg_tables_decode_schedule(const rk_tables *t, int32_t layer, int32_t *items, int64_t cap,
+                                        int64_t *n_items, int32_t *comb_off, int64_t comb_cap) {
+  if (!t) return fail(RK_ERR_INVALID_ARG, "null tables");
+  if (layer < t->layer_begin || layer >= t->layer_end) return fail(RK_ERR_INVALID_ARG, "layer outside the tables");
+  if (!t->decode_shaped) {
+    if (n_items) *n_items = 0;
+    return RK_OK;
+  }
+  const std::vector<rk::DecItem> &v = t->dec_items[layer - t->layer_begin];
+  const std::vector<int32_t> &c = t->dec_comb[layer - t->layer_begin];
+  if (n_items) *n_items = (int64_t)v.size();
+  if (items)
+    for (int64_t i = 0; i < std::min<int64_t>(cap, (int64_t)v.size()); ++i) {
+      items[4 * i + 0] = v[i].seq;
+      items[4 * i + 1] = v[i].kv_head;
+      items[4 * i + 2] = v[i].k0;
+      items[4 * i + 3] = v[i].k1;
+    }
+  if (comb_off)
+    for (int64_t i = 0; i < std::min<int64_t>(comb_cap, (int64_t)c.size()); ++i) comb_off[i] = c[i];
   return RK_OK;
 }
 
@@ -895,6 +1101,53 @@ rk_status rk_seg_key_mass(rk_pool *pool, const rk_tables *t, int32_t layer, cons
   p.n_units = (int32_t)units.size();
   hipError_t e = rk::launch_key_mass(p, pool->desc.head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "key mass kernel launch");
+  return RK_OK;
+  RK_GUARD_END
+}
+
+rk_status rk_seg_attn_decode(rk_pool *pool, const rk_tables *t, int32_t layer, const void *q, const void *k_new,
+                             const void *v_new, void *o, float *lse, float softmax_scale, void *stream) {
+  RK_GUARD_BEGIN
+  rk_status st = check_device_tables(pool, t, layer);
+  if (st != RK_OK) return st;
+  if (pool->desc.dtype != RK_BF16) return fail(RK_ERR_UNSUPPORTED, "decode needs a bf16 pool");
+  if (t->G > 16) return fail(RK_ERR_UNSUPPORTED, "decode supports at most 16 q heads per KV head");
+  if (!t->decode_shaped)
+    return fail(RK_ERR_STATE, "decode needs tables whose sequences have at most one query row each");
+  const int64_t total_q = t->cu_q[t->num_seqs];
+  if (total_q == 0) return RK_OK;
+  if (!q || !o || !aligned16(q) || !aligned16(o)) return fail(RK_ERR_INVALID_ARG, "q / o null or not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(RK_ERR_INVALID_ARG, "lse not 4-byte aligned");
+  if (!(softmax_scale <= 0.0f) && !std::isfinite(softmax_scale)) return fail(RK_ERR_INVALID_ARG, "softmax_scale not finite");
+  st = append_impl(pool, t, layer, k_new, v_new, stream);
+  if (st != RK_OK) return st;
+  const int32_t li = layer - t->layer_begin;
+  const rk_tables::LayerDev &d = t->dev[li];
+  rk::DecodeParams p{};
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  p.k_pages = pool->desc.k_pages;
+  p.v_pages = pool->desc.v_pages;
+  p.page_base = d.page_base;
+  p.page_ids = d.page_ids;
+  p.seqs = t->d_seqs;
+  p.items = d.dec_items;
+  p.comb_off = d.dec_comb;
+  p.part_o = t->d_part_o;
+  p.part_lse = t->d_part_lse;
+  p.num_seqs = t->num_seqs;
+  p.H = t->H;
+  p.Hkv = t->Hkv;
+  p.G = t->G;
+  p.P = t->P;
+  p.log2P = log2i(t->P);
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)pool->desc.head_dim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.total_q = (int32_t)total_q;
+  p.n_items = (int32_t)t->dec_items[li].size();
+  hipError_t e = rk::launch_decode(p, pool->desc.head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   return RK_OK;
   RK_GUARD_END
 }

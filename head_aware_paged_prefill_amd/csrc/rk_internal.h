@@ -155,7 +155,42 @@ struct MassParams {
 constexpr int kMassRun = 16;         // units placed together on one XCD
 constexpr int kMassChunkSteps = 64;  // steps per query chunk
 
+// Decode (one query row per sequence): split-KV work items, one wave each, over key ranges of the
+// query's visible set; the partial (o, lse) of item i go to slot i and are merged per (seq, kv head)
+// by the combine kernel.
+constexpr int kDecodeTargetItems = 2048;  // items per layer the key chunk aims at (8 waves per CU)
+constexpr int kDecodeMinChunk = 256;      // keys
+struct DecItem {
+  int32_t seq;
+  int32_t kv_head;
+  int32_t k0, k1;  // key range [k0, k1) of the sequence, all visible to its query
+};
+struct DecodeParams {
+  const void *q;       // [total_q][H][D] bf16
+  void *o;             // [total_q][H][D] bf16
+  float *lse;          // [H][total_q] or null
+  const void *k_pages;
+  const void *v_pages;
+  const int32_t *page_base;
+  const int32_t *page_ids;
+  const SeqInfo *seqs;
+  const DecItem *items;   // slot order: grouped by (seq, kv head), ranges ascending
+  const int32_t *comb_off;  // [num_seqs * Hkv + 1]: first slot of (seq, kv head) = b * Hkv + g
+  float *part_o;          // [n_items][G][D] fp32, normalised partial outputs
+  float *part_lse;        // [n_items][G] fp32, natural log
+  int32_t num_seqs;
+  int32_t H;
+  int32_t Hkv;
+  int32_t G;
+  int32_t P;
+  int32_t log2P;
+  float scale_log2;
+  int32_t total_q;
+  int32_t n_items;
+};
+
 hipError_t launch_attention(const AttnParams &p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_key_mass(const MassParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_append(const KvWriteParams &p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_import(const KvWriteParams &p, int n_pages, int dtype, int head_dim, hipStream_t stream);

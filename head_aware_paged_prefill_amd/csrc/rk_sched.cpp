@@ -167,4 +167,55 @@ void mass_schedule(const SchedInput &t, int32_t keys, int32_t tokens, std::vecto
   while (!units.empty() && units.back().seq < 0) units.pop_back();
 }
 
+namespace {
+// visible key ranges of the query at position L - 1 of one (kv head, seq); returns their number
+int decode_ranges(int cls, int32_t L, int32_t S, int32_t W, int32_t r[4]) {
+  if (L <= 0) return 0;
+  if (cls == RK_GLOBAL) {
+    r[0] = 0, r[1] = L;
+    return 1;
+  }
+  const int32_t s1 = std::min(S, L), w0 = std::max(0, L - W);
+  if (s1 >= w0) {
+    r[0] = 0, r[1] = L;
+    return 1;
+  }
+  int n = 0;
+  if (s1 > 0) r[2 * n] = 0, r[2 * n + 1] = s1, ++n;
+  r[2 * n] = w0, r[2 * n + 1] = L, ++n;
+  return n;
+}
+}  // namespace
+
+// A range of n keys cut at multiples of the chunk gives at most n / chunk + 2 items, and keys / chunk
+// <= kDecodeTargetItems; a (seq, kv head) has at most two ranges.
+int64_t decode_items_bound(const SchedInput &t) { return kDecodeTargetItems + 4 * (int64_t)t.num_seqs * t.Hkv; }
+
+void decode_schedule(const SchedInput &t, std::vector<DecItem> &items, std::vector<int32_t> &comb_off) {
+  items.clear();
+  comb_off.assign((size_t)t.num_seqs * t.Hkv + 1, 0);
+  int64_t keys = 0;
+  int32_t r[4];
+  for (int32_t b = 0; b < t.num_seqs; ++b) {
+    if (t.kv_len[b] - t.q_begin[b] != 1) continue;  // no query row
+    for (int32_t g = 0; g < t.Hkv; ++g) {
+      const int n = decode_ranges(t.head_class[g], t.kv_len[b], t.sink, t.window, r);
+      for (int i = 0; i < n; ++i) keys += r[2 * i + 1] - r[2 * i];
+    }
+  }
+  int64_t chunk = (keys + kDecodeTargetItems - 1) / kDecodeTargetItems;
+  chunk = std::max<int64_t>(kDecodeMinChunk, (chunk + 31) / 32 * 32);
+  for (int32_t b = 0; b < t.num_seqs; ++b)
+    for (int32_t g = 0; g < t.Hkv; ++g) {
+      comb_off[(size_t)b * t.Hkv + g] = (int32_t)items.size();
+      if (t.kv_len[b] - t.q_begin[b] != 1) continue;
+      const int n = decode_ranges(t.head_class[g], t.kv_len[b], t.sink, t.window, r);
+      for (int i = 0; i < n; ++i)
+        for (int64_t c = r[2 * i] / chunk; c * chunk < r[2 * i + 1]; ++c)
+          items.push_back({b, g, (int32_t)std::max<int64_t>(r[2 * i], c * chunk),
+                           (int32_t)std::min<int64_t>(r[2 * i + 1], (c + 1) * chunk)});
+    }
+  comb_off[(size_t)t.num_seqs * t.Hkv] = (int32_t)items.size();
+}
+
 }  // namespace rk

@@ -32,8 +32,9 @@ EXPORTS = [
     "rk_seg_pool_create", "rk_seg_pool_destroy", "rk_seg_pool_query", "rk_seg_pool_free_list",
     "rk_seg_tables_workspace_bytes", "rk_seg_build_tables", "rk_seg_tables_export", "rk_seg_tables_schedule",
     "rk_seg_tables_mass_schedule", "rk_seg_tables_stats", "rk_seg_tables_trim", "rk_seg_tables_destroy", "rk_seg_reuse_rerotate",
-    "rk_seg_append_kv", "rk_seg_attn_prefill", "rk_seg_key_mass", "rk_status_string", "rk_last_error",
-    "rk_seg_version",
+    "rk_seg_append_kv", "rk_seg_attn_prefill", "rk_seg_key_mass", "rk_seg_tables_advance_workspace_bytes",
+    "rk_seg_tables_advance", "rk_seg_tables_decode_schedule", "rk_seg_attn_decode", "rk_status_string",
+    "rk_last_error", "rk_seg_version",
 ]
 
 
@@ -93,6 +94,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rk_seg_append_kv": [VP, VP, I32, VP, VP, VP],
         "rk_seg_attn_prefill": [VP, VP, I32, VP, VP, VP, VP, VP, ctypes.c_float, VP],
         "rk_seg_key_mass": [VP, VP, I32, VP, VP, VP, ctypes.c_float, VP],
+        "rk_seg_tables_advance_workspace_bytes": [VP, VP, P(I32), P(ctypes.c_size_t)],
+        "rk_seg_tables_advance": [VP, VP, P(I32), VP, ctypes.c_size_t, VP],
+        "rk_seg_tables_decode_schedule": [VP, I32, P(I32), I64, P(I64), P(I32), I64],
+        "rk_seg_attn_decode": [VP, VP, I32, VP, VP, VP, VP, VP, ctypes.c_float, VP],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -343,6 +348,62 @@ def rk_seg_key_mass(tables: Tables, layer: int, q, lse, mass, softmax_scale: flo
     fp32 it returned; mass: [H][sum kv_len] fp32, written for every key."""
     _check(load().rk_seg_key_mass(tables.pool.handle, tables.handle, layer, _ptr(q), _ptr(lse), _ptr(mass),
                                   float(softmax_scale), _stream(stream)))
+
+
+def rk_seg_tables_advance_workspace_bytes(tables: Tables, n_new) -> int:
+    nn = _i32(n_new)
+    n = ctypes.c_size_t()
+    _check(load().rk_seg_tables_advance_workspace_bytes(tables.pool.handle, tables.handle,
+                                                        nn.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                                        ctypes.byref(n)))
+    return n.value
+
+
+def rk_seg_tables_advance(tables: Tables, n_new, device=True, workspace=None, stream=None) -> Tables:
+    """The next call on the same sequences: sequence b gains n_new[b] tokens (its query rows).  With
+    device=True the device view goes into `workspace` (a uint8 tensor, reused when large enough) or
+    into a new one.  Returns `tables` (the same handle)."""
+    L = load()
+    nn = _i32(n_new)
+    pn = nn.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    ws_ptr, ws_bytes, st = None, 0, None
+    if device:
+        import torch
+        need = rk_seg_tables_advance_workspace_bytes(tables, nn)
+        if workspace is None:
+            workspace = tables.workspace
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(256, need), dtype=torch.uint8, device="cuda")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        st = _stream(stream)
+    _check(L.rk_seg_tables_advance(tables.pool.handle, tables.handle, pn, ws_ptr, ws_bytes, st))
+    tables.workspace = workspace if device else None
+    tables._keep = tables._keep + (nn,)
+    return tables
+
+
+def rk_seg_tables_decode_schedule(tables: Tables, layer: int):
+    """(items [n][4] = (seq, kv head, k0, k1), comb_off [num_seqs * Hkv + 1] or None when not decode-shaped)."""
+    L = load()
+    n = ctypes.c_int64()
+    _check(L.rk_seg_tables_decode_schedule(tables.handle, layer, None, 0, ctypes.byref(n), None, 0))
+    if n.value == 0:
+        return np.zeros((0, 4), np.int32), None
+    nb = int(tables.pool.desc.num_kv_heads) * len(tables._keep[0]) + 1
+    out = np.zeros((n.value, 4), np.int32)
+    comb = np.zeros(nb, np.int32)
+    _check(L.rk_seg_tables_decode_schedule(tables.handle, layer, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                           n.value, ctypes.byref(n), comb.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                           nb))
+    return out, comb
+
+
+def rk_seg_attn_decode(tables: Tables, layer: int, q, k_new, v_new, o, lse=None, softmax_scale: float = 0.0,
+                       stream=None) -> None:
+    """Decode: append (unless k_new and v_new are None), split-KV attention and combine.  q, o:
+    [total_q][H][D] bf16 (one row per sequence with a query); lse: [H][total_q] fp32."""
+    _check(load().rk_seg_attn_decode(tables.pool.handle, tables.handle, layer, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                     _ptr(o), _ptr(lse), float(softmax_scale), _stream(stream)))
 
 
 def rk_seg_version() -> str:

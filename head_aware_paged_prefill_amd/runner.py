@@ -81,6 +81,31 @@ class PrefillRunner:
         rk_seg.rk_seg_key_mass(self.tables, layer, q, lse, mass, scale, stream)
         return mass
 
+    def trim(self):
+        """After the call: LOCAL heads keep only what the next query sees (sink + window pages)."""
+        rk_seg.rk_seg_tables_trim(self.tables)
+
+    def advance(self, n_new, stream=None):
+        """The next call on the same sequences: sequence b gains n_new[b] tokens (its queries).  The
+        device view is rebuilt in the runner's workspace (grown when it is too small)."""
+        rk_seg.rk_seg_tables_advance(self.tables, n_new, device=True, workspace=self.workspace, stream=stream)
+        self.workspace = self.tables.workspace
+        return self.tables
+
+    def decode(self, q, k_new, v_new, o=None, lse=None, layer: Optional[int] = None, scale: float = 0.0,
+               stream=None):
+        """Decode on decode-shaped tables: q, k_new, v_new one row per sequence with a query
+        ([rows][H][D], [rows][Hkv][D]); returns o [rows][H][D] and lse [H][rows]."""
+        wl = self.wl
+        layer = wl.layer if layer is None else layer
+        rows = q.shape[0]
+        if o is None:
+            o = torch.empty((rows, wl.num_q_heads, wl.head_dim), dtype=wl.dtype, device=self.device)
+        if lse is None:
+            lse = torch.empty((wl.num_q_heads, rows), dtype=torch.float32, device=self.device)
+        rk_seg.rk_seg_attn_decode(self.tables, layer, q, k_new, v_new, o, lse, scale, stream)
+        return o, lse
+
     def release(self, trim: bool = True):
         if self.tables is not None:
             if trim:

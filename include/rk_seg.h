@@ -177,6 +177,27 @@ rk_status rk_seg_tables_workspace_bytes(const rk_pool *pool, const rk_batch_desc
 rk_status rk_seg_build_tables(rk_pool *pool, const rk_batch_desc *batch, void *d_workspace,
                               size_t ws_bytes, void *stream, rk_tables **out);
 
+/* The next call on the same sequences and layers (decode: one token each; or a further chunk):
+ * sequence b gains n_new[b] >= 0 tokens, which become its query rows (q_start = q_start_global =
+ * the old kv_len; kv_len += n_new[b]).  The pool's pages keep the state the previous call left:
+ * every (layer, KV head, seq) keeps the physical page, and its contents, of each logical page it
+ * still holds under the held-token rule of rk_seg_build_tables for the new q_start / kv_len; pages
+ * it no longer holds (a LOCAL head's window moving on) go back to the free list first, in ascending
+ * (layer, KV head, seq, logical page) order, then the new pages are taken from the head of the free
+ * list in the same order.  Works on trimmed and untrimmed tables; the result is untrimmed.  (Page
+ * "RedKnot – 小红书研发并开源的长上下文大模型推理引擎" (shshi.cn), section RedKnot核心特点: more
+ * concurrent long-context sessions per GPU, i.e. serving over the retained segmented state.)
+ * d_workspace: as for rk_seg_build_tables, >= rk_seg_tables_advance_workspace_bytes; it may be the
+ *   workspace the tables used before (the previous upload is waited for first).  NULL: host only.
+ * n_new: host [num_seqs].
+ * Errors: RK_ERR_INVALID_ARG, RK_ERR_OUT_OF_PAGES and RK_ERR_WORKSPACE_TOO_SMALL leave the tables
+ *   and the pool unchanged; RK_ERR_HIP on the upload leaves the new page state without a device
+ *   view (device calls then fail with RK_ERR_STATE). */
+rk_status rk_seg_tables_advance_workspace_bytes(const rk_pool *pool, const rk_tables *tables,
+                                                const int32_t *n_new, size_t *bytes);
+rk_status rk_seg_tables_advance(rk_pool *pool, rk_tables *tables, const int32_t *n_new,
+                                void *d_workspace, size_t ws_bytes, void *stream);
+
 /* Export the held segments and physical page ids of one (layer, KV head, seq), host side.
  * seg_tok_begin / seg_npages: [seg_cap]; page_ids: [page_cap], in logical page order.
  * *n_segs and *n_pages receive the full counts even when larger than the capacities. */
@@ -202,6 +223,18 @@ rk_status rk_seg_tables_schedule(const rk_tables *tables, int32_t layer, int32_t
 rk_status rk_seg_tables_mass_schedule(const rk_tables *tables, int32_t layer, int32_t *units, int64_t cap,
                                       int64_t *n_units, int32_t *keys_per_unit, int32_t *tokens_per_step,
                                       int32_t *steps_per_chunk);
+
+/* Export the split-KV decode items of one layer (rk_seg_attn_decode), in launch order: items
+ * [cap][4] = (seq, kv_head, k0, k1): the keys [k0, k1) of the sequence, all visible to its query
+ * (the token at kv_len - 1).  A (seq, kv head)'s visible keys are GLOBAL [0, kv_len) or LOCAL
+ * [0, min(sink, kv_len)) and [max(0, kv_len - window), kv_len) (merged when they touch), cut at
+ * multiples of one key chunk (a multiple of 32, at least 256).  Items come grouped by (seq, kv
+ * head), ascending; comb_off [comb_cap] receives the first item of (seq b, kv head g) at
+ * b * num_kv_heads + g and the item count at num_seqs * num_kv_heads.  *n_items = 0 when the tables
+ * are not decode-shaped (a sequence with more than one query row, or more than 16 q heads per KV
+ * head).  Any output pointer may be NULL. */
+rk_status rk_seg_tables_decode_schedule(const rk_tables *tables, int32_t layer, int32_t *items, int64_t cap,
+                                        int64_t *n_items, int32_t *comb_off, int64_t comb_cap);
 
 rk_status rk_seg_tables_stats(const rk_tables *tables, rk_tables_stats *out);
 
@@ -266,6 +299,22 @@ rk_status rk_seg_attn_prefill(rk_pool *pool, const rk_tables *tables, int32_t la
  * KV head, more than 2^31 keys), RK_ERR_HIP. */
 rk_status rk_seg_key_mass(rk_pool *pool, const rk_tables *tables, int32_t layer, const void *q,
                           const float *lse, float *mass, float softmax_scale, void *stream);
+
+/* Decode for one layer of decode-shaped tables (every sequence has at most one query row, at
+ * position kv_len - 1, e.g. after rk_seg_tables_advance with n_new = 1): append k_new / v_new
+ * (as rk_seg_append_kv; skipped when both are NULL), then split-KV attention over the items of
+ * rk_seg_tables_decode_schedule, each giving a partial (o_s, lse_s) over its key range, then the
+ * combine o = sum_s e^{lse_s - lse} o_s, lse = log sum_s e^{lse_s} into o / lse.  The result is the
+ * masked softmax attention of rk_seg_attn_prefill for those rows.
+ * q, o: device [total_q][num_q_heads][head_dim] bf16 (total_q = the sequences with a query row);
+ * lse: device [num_q_heads][total_q] fp32 or NULL; softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * The partials live in the tables' workspace, so decode calls on one tables object are ordered on
+ * one stream.
+ * Errors: RK_ERR_UNSUPPORTED for fp32 pools or more than 16 q heads per KV head; RK_ERR_STATE for
+ *   tables that are not decode-shaped, trimmed or host-only; RK_ERR_INVALID_ARG; RK_ERR_HIP. */
+rk_status rk_seg_attn_decode(rk_pool *pool, const rk_tables *tables, int32_t layer, const void *q,
+                             const void *k_new, const void *v_new, void *o, float *lse,
+                             float softmax_scale, void *stream);
 
 /* -- diagnostics --------------------------------------------------------------------------- */
 

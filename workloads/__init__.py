@@ -305,6 +305,16 @@ class Inputs:
     boost: List[np.ndarray]  # per seq bool [Hkv][kv_len]
 
 
+def decode_inputs(wl: Workload, step: int, rows: int, device: str | torch.device = "cpu"):
+    """The new token of each decoding sequence at decode step `step`: q [rows][H][D], k, v
+    [rows][Hkv][D], seeded normal draws in the workload's dtype."""
+    base = wl.seed(SEED_Q) * 104729 + 7 * step
+    q = normal(base + 1, (rows, wl.num_q_heads, wl.head_dim), wl.dtype, device)
+    k = normal(base + 2, (rows, wl.num_kv_heads, wl.head_dim), wl.dtype, device)
+    v = normal(base + 3, (rows, wl.num_kv_heads, wl.head_dim), wl.dtype, device)
+    return q, k, v
+
+
 def pool_pages_needed_hint(wl: Workload) -> int:
     """An upper bound on the pages one call holds: every (kv head, seq) holding its whole context."""
     P = wl.page_size
