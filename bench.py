@@ -149,9 +149,51 @@ def time_key_mass(b: "Bench", reps: int) -> dict:
     return {"ms": ms, "tflops": tf, "pct_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS}
 
 
+def time_decode(b: "Bench", reps: int) -> dict:
+    """Time one decode step over the state the call leaves: after the prefill call and trim, every
+    sequence advances by one token (rk_seg_tables_advance, host + upload, untimed), then
+    rk_seg_attn_decode (append the token, split-KV attention, combine) is timed with HIP events on
+    the stream it runs on.  Algorithmic bytes: K and V of every key a decode query sees (per KV head)
+    plus q and o; the kernel reads each of them once."""
+    wl, r = b.wl, b.r
+    r.build()
+    r.import_docs(b.inp.docs)
+    rk_seg.rk_seg_append_kv(r.tables, wl.layer, b.inp.k_new, b.inp.v_new)
+    rk_seg.rk_seg_attn_prefill(r.tables, wl.layer, b.inp.q, None, None, b.o, b.lse)
+    r.trim()
+    B = wl.num_seqs
+    r.advance([1] * B)
+    q, k, v = workloads.decode_inputs(wl, 0, B, device="cuda")
+    o = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=wl.dtype, device="cuda")
+    lse = torch.empty((wl.num_q_heads, B), dtype=torch.float32, device="cuda")
+    rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, k, v, o, lse)  # the append is idempotent
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, k, v, o, lse)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    items, _ = rk_seg.rk_seg_tables_decode_schedule(r.tables, wl.layer)
+    keys = int((items[:, 3] - items[:, 2]).sum())
+    elem = 2 if wl.dtype == torch.bfloat16 else 4
+    nbytes = keys * 2 * wl.head_dim * elem + 2 * B * wl.num_q_heads * wl.head_dim * elem
+    dense_bytes = sum(L + 1 for L in wl.kv_lens) * wl.num_kv_heads * 2 * wl.head_dim * elem \
+        + 2 * B * wl.num_q_heads * wl.head_dim * elem
+    r.release(trim=True)
+    ms = float(np.median(ts))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": ms, "gbs": gbs, "pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS, "bytes": nbytes,
+            "dense_bytes": dense_bytes, "items": int(len(items))}
+
+
 def run_workload(wl, steps: int, warmup: int, with_dense: bool):
     log("workload: %s" % wl.name)
-    inp = workloads.make_inputs(wl, device="cuda")
+    # room for the decode step's new pages (one per (seq, kv head) at most)
+    pages = workloads.pool_pages_needed_hint(wl) + wl.pool_slack + 2 * wl.num_seqs * wl.num_kv_heads
+    inp = workloads.make_inputs(wl, device="cuda", num_pages=pages)
     runner = PrefillRunner(wl, free_order=inp.free_order, poison=True)
     b = Bench(wl, inp, runner)
     ms_step = b.run(steps, warmup)
@@ -177,11 +219,18 @@ def run_workload(wl, steps: int, warmup: int, with_dense: bool):
         res["key_mass"] = time_key_mass(b, max(2, steps // 2))
         log("  per-key mass pass: %.3f ms, %.1f useful TFLOP/s (QK half, %.1f%% of bf16 peak)" % (
             res["key_mass"]["ms"], res["key_mass"]["tflops"], res["key_mass"]["pct_mfma_peak"]))
+    if wl.group <= 16 and wl.dtype == torch.bfloat16:
+        res["decode"] = time_decode(b, 20)
+        log("  decode step (one token per sequence): %.3f ms, %.0f GB/s algorithmic (%.1f%% of HBM peak), "
+            "%.1f MB read of %.1f MB dense (%.2fx fewer)" % (
+                res["decode"]["ms"], res["decode"]["gbs"], res["decode"]["pct_hbm_peak"], res["decode"]["bytes"] / 1e6,
+                res["decode"]["dense_bytes"] / 1e6, res["decode"]["dense_bytes"] / res["decode"]["bytes"]))
     if with_dense:
         wl_d = wl.with_classes(np.ones_like(wl.head_class), wl.name + " all-global")
         bd = Bench(wl_d, dataclasses.replace(inp, wl=wl_d), runner)
         bd.r.wl = wl_d
         ms_d = bd.run(max(1, steps // 2), 1)
+        dec_d = time_decode(bd, 10) if "decode" in res else None
         runner.wl = wl
         fd = useful_flops(bd.stats, wl.head_dim)
         res["dense_reference"] = {
@@ -189,6 +238,10 @@ def run_workload(wl, steps: int, warmup: int, with_dense: bool):
             "tflops_attention": fd / (float(np.mean(bd.attn_ms)) * 1e-3) / 1e12,
             "pct_mfma_peak_attention": 100.0 * fd / (float(np.mean(bd.attn_ms)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         }
+        if dec_d is not None:
+            res["dense_reference"]["decode"] = dec_d
+            log("  dense reference decode step: %.3f ms, %.0f GB/s algorithmic (%.1f%% of HBM peak)" % (
+                dec_d["ms"], dec_d["gbs"], dec_d["pct_hbm_peak"]))
         res["dense_over_mixed_time"] = res["dense_reference"]["ms_attention"] / res["ms_attention"]
         res["dense_over_mixed_pairs"] = fd / flops
         log("  dense reference: attention %.3f ms, %.1f TFLOP/s (%.1f%%)" % (

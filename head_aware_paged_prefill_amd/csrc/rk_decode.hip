@@ -10,8 +10,8 @@
 //    tile give each lane the 8 keys its B operand needs, in the order the V loads follow).  K and V
 //    come straight from the pages into registers (16- and 8-byte loads off a scalar page base), one
 //    32-key tile ahead.  Online softmax in fp32; the item writes its normalised partial output and lse.
-//  * decode_combine<D>: merges the partials of each (seq, kv head): lse = log sum_s e^{lse_s},
-//    o = sum_s e^{lse_s - lse} o_s (the split-KV combine).
+//  * decode_combine<D>: merges the partials of each query row: lse = log sum_s e^{lse_s},
+//    o = sum_s e^{lse_s - lse} o_s (the split-KV combine), one workgroup per row.
 // Decode reads every visible K/V byte once, so it is bound by HBM bandwidth, not by the MFMAs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -24,6 +24,21 @@ namespace rk {
 namespace {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// max / sum over the four 16-lane groups (lanes c16, c16 + 16, c16 + 32, c16 + 48), with lane swaps
+// (no LDS traffic)
+__device__ __forceinline__ float groups_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float groups_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D>
 struct DecTile {
@@ -48,6 +63,11 @@ __global__ void __launch_bounds__(64) decode_bf16(DecodeParams p) {
     const int pg = pt[min(key, L - 1) >> p.log2P];
     return key < L && pg >= 0 ? pg : pg0;
   };
+  // page ids of a tile's two 16-key halves, looked up two tiles before its loads are issued
+  struct Pages {
+    int a, b;
+  };
+  auto pages_of = [&](int kt) { return Pages{page_of(kt), page_of(kt + 16)}; };
 
   // Q as the B operand of S^T: lane holds channels 32 ks + 8 q4 .. + 7 of row c16 (q head g G + c16)
   bf16x8 qf[KS];
@@ -65,22 +85,22 @@ __global__ void __launch_bounds__(64) decode_bf16(DecodeParams p) {
   const char *vbytes = static_cast<const char *>(p.v_pages);
   const uint32_t k_lane = (uint32_t)((c16 * D + 8 * q4) * 2);  // bytes within a 16-key block of a K page
   const uint32_t v_lane = (uint32_t)((c16 * P + 4 * q4) * 2);  // bytes within a 16-channel block of a V page
-  auto load = [&](int kt, DecTile<D> &T) {
-    const int pa = page_of(kt), pb = page_of(kt + 16);  // uniform; equal when P >= 32
+  auto load = [&](int kt, Pages pg, DecTile<D> &T) {  // pg: uniform; a == b when P >= 32
     const int sa = kt & (P - 1), sb = (kt + 16) & (P - 1);
-    const char *ka = kbytes + ((int64_t)pa * P + sa) * D * 2;
-    const char *kb = kbytes + ((int64_t)pb * P + sb) * D * 2;
+    const char *ka = kbytes + ((int64_t)pg.a * P + sa) * D * 2;
+    const char *kb = kbytes + ((int64_t)pg.b * P + sb) * D * 2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      T.k[0][ks] = *reinterpret_cast<const bf16x8 *>(ka + opaque(k_lane) + 64 * ks);
-      T.k[1][ks] = *reinterpret_cast<const bf16x8 *>(kb + opaque(k_lane) + 64 * ks);
+      T.k[0][ks] = *reinterpret_cast<const bf16x8 *>(ka + 64 * ks + opaque(k_lane));
+      T.k[1][ks] = *reinterpret_cast<const bf16x8 *>(kb + 64 * ks + opaque(k_lane));
     }
-    const char *va = vbytes + ((int64_t)pa * D * P + sa) * 2;
-    const char *vb = vbytes + ((int64_t)pb * D * P + sb) * 2;
+    const char *va = vbytes + ((int64_t)pg.a * D * P + sa) * 2;
+    const char *vb = vbytes + ((int64_t)pg.b * D * P + sb) * 2;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      T.va[dt] = *reinterpret_cast<const u32x2 *>(va + opaque(v_lane) + dt * 16 * P * 2);
-      T.vb[dt] = *reinterpret_cast<const u32x2 *>(vb + opaque(v_lane) + dt * 16 * P * 2);
+      const int64_t row = (int64_t)dt * 16 * P * 2;  // uniform: the dt-th 16-channel block
+      T.va[dt] = *reinterpret_cast<const u32x2 *>(va + row + opaque(v_lane));
+      T.vb[dt] = *reinterpret_cast<const u32x2 *>(vb + row + opaque(v_lane));
     }
   };
 
@@ -111,8 +131,7 @@ __global__ void __launch_bounds__(64) decode_bf16(DecodeParams p) {
         x[4 * h + i] = v;
         mt = fmaxf(mt, v);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = groups_max(mt);
     const float mn = fmaxf(m, mt);
     const float alpha = fast_exp2(m - mn);
     m = mn;
@@ -133,22 +152,30 @@ __global__ void __launch_bounds__(64) decode_bf16(DecodeParams p) {
     }
   };
 
+  // tile t's loads are issued while tile t - 1 is computed; its page ids were looked up two tiles
+  // earlier (scalar loads stay in flight: no LDS instruction shares their wait counter)
   const int t0 = k0 & ~31;
   const int ntiles = ((k1 - 1 - t0) >> 5) + 1;
   DecTile<D> buf[2];
-  load(t0, buf[0]);
+  Pages pn = pages_of(t0), pn2 = pages_of(t0 + 32);
+  load(t0, pn, buf[0]);
+  pn = pn2;
+  pn2 = pages_of(t0 + 64);
   for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) load(t0 + 32 * (t + 1), buf[1]);
+    if (t + 1 < ntiles) load(t0 + 32 * (t + 1), pn, buf[1]);
+    pn = pn2;
+    pn2 = pages_of(t0 + 32 * (t + 3));
     compute(t0 + 32 * t, buf[0]);
     if (t + 1 < ntiles) {
-      if (t + 2 < ntiles) load(t0 + 32 * (t + 2), buf[0]);
+      if (t + 2 < ntiles) load(t0 + 32 * (t + 2), pn, buf[0]);
+      pn = pn2;
+      pn2 = pages_of(t0 + 32 * (t + 4));
       compute(t0 + 32 * (t + 1), buf[1]);
     }
   }
 
   // row sum over the four lane groups; normalised partial output and lse (natural log)
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = groups_sum(l);
   if (c16 < G) {
     const float inv = 1.0f / l;
     float *po = p.part_o + ((int64_t)blockIdx.x * G + c16) * D + 4 * q4;
@@ -158,29 +185,54 @@ __global__ void __launch_bounds__(64) decode_bf16(DecodeParams p) {
   }
 }
 
-// One workgroup per (seq, kv head): lse = max + log sum_s e^{lse_s - max}; o = sum_s e^{lse_s - lse} o_s.
+// One workgroup per query row (seq, q head): lse = max + log sum_s e^{lse_s - max} and
+// o = sum_s e^{lse_s - lse} o_s over the row's partials s.  The partials are spread over NG groups
+// of D / 4 threads (each thread four channels), which are summed through LDS at the end.
 template <int D>
 __global__ void __launch_bounds__(256) decode_combine(DecodeParams p) {
-  const int bg = blockIdx.x;
+  constexpr int TPG = D / 4;         // threads per group: one 16-byte chunk of a partial each
+  constexpr int NG = 256 / TPG;      // groups
+  __shared__ float red[256];
+  __shared__ f32x4 part[NG][TPG];
+  const int tid = threadIdx.x;
+  const int G = p.G;
+  const int bg = blockIdx.x / G, r = blockIdx.x - bg * G;
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
   const int s0 = p.comb_off[bg], s1 = p.comb_off[bg + 1];
   if (s0 == s1) return;  // the sequence has no query row
   const SeqInfo si = p.seqs[b];
-  const int G = p.G;
-  for (int e = threadIdx.x; e < G * (D / 4); e += blockDim.x) {
-    const int r = e / (D / 4), d4 = e - r * (D / 4);
-    float mx = -INFINITY;
-    for (int s = s0; s < s1; ++s) mx = fmaxf(mx, p.part_lse[(int64_t)s * G + r]);
-    float tot = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = s0; s < s1; ++s) {
-      const float w = expf(p.part_lse[(int64_t)s * G + r] - mx);
-      tot += w;
-      acc += w * *reinterpret_cast<const f32x4 *>(p.part_o + ((int64_t)s * G + r) * D + 4 * d4);
+  auto block_reduce = [&](float v, bool is_max) {
+    red[tid] = v;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (tid < w) red[tid] = is_max ? fmaxf(red[tid], red[tid + w]) : red[tid] + red[tid + w];
+      __syncthreads();
     }
+    const float out = red[0];
+    __syncthreads();
+    return out;
+  };
+  float mx = -INFINITY;
+  for (int s = s0 + tid; s < s1; s += 256) mx = fmaxf(mx, p.part_lse[(int64_t)s * G + r]);
+  mx = block_reduce(mx, true);
+  float tot = 0.f;
+  for (int s = s0 + tid; s < s1; s += 256) tot += expf(p.part_lse[(int64_t)s * G + r] - mx);
+  tot = block_reduce(tot, false);
+  const float lse = mx + logf(tot);
+  const int grp = tid / TPG, d4 = tid - grp * TPG;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = s0 + grp; s < s1; s += NG) {
+    const float w = expf(p.part_lse[(int64_t)s * G + r] - lse);
+    acc += w * *reinterpret_cast<const f32x4 *>(p.part_o + ((int64_t)s * G + r) * D + 4 * d4);
+  }
+  part[grp][d4] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    for (int j = 1; j < NG; ++j) acc += part[j][d4];
     const int64_t row = (int64_t)si.cu_q * p.H + g * G + r;
-    *reinterpret_cast<bf16x4 *>(static_cast<bf16_t *>(p.o) + row * D + 4 * d4) = __builtin_convertvector(acc / tot, bf16x4);
-    if (d4 == 0 && p.lse) p.lse[(int64_t)(g * G + r) * p.total_q + si.cu_q] = mx + logf(tot);
+    *reinterpret_cast<bf16x4 *>(static_cast<bf16_t *>(p.o) + row * D + 4 * d4) = __builtin_convertvector(acc, bf16x4);
+    if (d4 == 0 && p.lse) p.lse[(int64_t)(g * G + r) * p.total_q + si.cu_q] = lse;
   }
 }
 
@@ -188,7 +240,7 @@ __global__ void __launch_bounds__(256) decode_combine(DecodeParams p) {
 
 hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t stream) {
   if (p.n_items <= 0) return hipSuccess;
-  const dim3 grid((unsigned)p.n_items), comb((unsigned)(p.num_seqs * p.Hkv));
+  const dim3 grid((unsigned)p.n_items), comb((unsigned)(p.num_seqs * p.Hkv * p.G));
   if (head_dim == 128) {
     hipLaunchKernelGGL(decode_bf16<128>, grid, dim3(64), 0, stream, p);
     hipLaunchKernelGGL(decode_combine<128>, comb, dim3(256), 0, stream, p);

@@ -194,16 +194,20 @@ int64_t decode_items_bound(const SchedInput &t) { return kDecodeTargetItems + 4 
 void decode_schedule(const SchedInput &t, std::vector<DecItem> &items, std::vector<int32_t> &comb_off) {
   items.clear();
   comb_off.assign((size_t)t.num_seqs * t.Hkv + 1, 0);
-  int64_t keys = 0;
+  int64_t keys = 0, ranges = 0;
   int32_t r[4];
   for (int32_t b = 0; b < t.num_seqs; ++b) {
     if (t.kv_len[b] - t.q_begin[b] != 1) continue;  // no query row
     for (int32_t g = 0; g < t.Hkv; ++g) {
       const int n = decode_ranges(t.head_class[g], t.kv_len[b], t.sink, t.window, r);
+      ranges += n;
       for (int i = 0; i < n; ++i) keys += r[2 * i + 1] - r[2 * i];
     }
   }
-  int64_t chunk = (keys + kDecodeTargetItems - 1) / kDecodeTargetItems;
+  // a range gives at most len / chunk + 2 items: leave room for them, so that the items fit one
+  // round of resident waves where they can
+  const int64_t room = std::max<int64_t>(kDecodeTargetItems / 4, kDecodeTargetItems - 2 * ranges);
+  int64_t chunk = (keys + room - 1) / room;
   chunk = std::max<int64_t>(kDecodeMinChunk, (chunk + 31) / 32 * 32);
   for (int32_t b = 0; b < t.num_seqs; ++b)
     for (int32_t g = 0; g < t.Hkv; ++g) {

@@ -36,7 +36,8 @@ int64_t mass_units_bound(const SchedInput &in, int32_t keys, int32_t tokens);
 // Decode-shaped calls (every sequence has at most one query row, at position kv_len - 1): split-KV
 // items over the query's visible key ranges (GLOBAL: [0, L); LOCAL: [0, min(S, L)) and
 // [max(0, L - W), L), merged when they touch).  A range is cut at multiples of the key chunk, which
-// aims the layer at kDecodeTargetItems items (at least kDecodeMinChunk keys, a multiple of 32).
+// keeps the layer within kDecodeTargetItems items, two per range reserved for the cuts that do not
+// fall on a range boundary (at least kDecodeMinChunk keys, a multiple of 32).
 // Items come grouped by (seq, kv head) in ascending key order; comb_off[b * Hkv + g] is the first
 // item of (b, g) and comb_off[num_seqs * Hkv] the item count.
 void decode_schedule(const SchedInput &in, std::vector<DecItem> &items, std::vector<int32_t> &comb_off);

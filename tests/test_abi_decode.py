@@ -98,6 +98,13 @@ def _decode_case(rng):
     return dict(Hkv=Hkv, G=G, P=P, kv=kv, S=S, W=W, hc=hc)
 
 
+def _ranges(cls, L, S, W):
+    """Visible key ranges of the query at L - 1, counted from the mask (runs of visible keys)."""
+    vis = attention.visibility_mask(cls, np.array([L - 1]), L, S, W)[0].astype(np.int8)
+    edges = np.flatnonzero(np.diff(np.concatenate([[0], vis, [0]])))
+    return list(zip(edges[::2], edges[1::2]))
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_decode_items_cover_the_visible_keys_once(seed):
     rng = np.random.Generator(np.random.PCG64(4400 + seed))
@@ -134,7 +141,11 @@ def test_decode_items_cover_the_visible_keys_once(seed):
     # a multiple of it
     keys = sum(int(attention.visibility_mask(int(c["hc"][0, g]), np.array([L - 1]), L, c["S"], c["W"]).sum())
                for b, L in enumerate(c["kv"]) if n_new[b] for g in range(Hkv))
-    chunk = max(256, -(-(-(-keys // 2048)) // 32) * 32)
+    ranges = sum(len(_ranges(int(c["hc"][0, g]), L, c["S"], c["W"])) for b, L in enumerate(c["kv"]) if n_new[b]
+                 for g in range(Hkv))
+    room = max(2048 // 4, 2048 - 2 * ranges)
+    chunk = max(256, -(-(-(-keys // room)) // 32) * 32)
+    assert len(items) <= 2048 or room == 2048 // 4
     for _, _, k0, k1 in items.tolist():
         assert k0 // chunk == (k1 - 1) // chunk
     rk_seg.rk_seg_tables_destroy(t)
