@@ -162,6 +162,8 @@ struct rk_tables {
   std::vector<LayerDev> dev;
   const rk::SeqInfo *d_seqs = nullptr;
   float *d_part_o = nullptr, *d_part_lse = nullptr;  // decode partials, shared by the layers
+  const int32_t *d_pack_ids = nullptr;  // held pages in (seq, layer, kv head, logical page) order
+  std::vector<int64_t> pack_off;        // [num_seqs + 1]: first packed page of each sequence
   StagingBuf staging;
   hipEvent_t ev = nullptr;
   bool trimmed = false;
@@ -181,6 +183,7 @@ struct WsLayout {
   size_t seqs = 0;
   std::vector<size_t> page_base, page_ids, head_class, items, app, mass, dec_items, dec_comb;
   size_t part_o = 0, part_lse = 0;  // decode-shaped calls only
+  size_t pack_ids = 0;              // the held pages in hand-off order
   size_t total = 0;
 };
 
@@ -295,6 +298,8 @@ WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, CallSched *sched)
     w.part_lse = off;
     off = align_up(off + sizeof(float) * dec_bound * G);
   }
+  w.pack_ids = off;  // at most every logical page of every (layer, kv head, seq)
+  off = align_up(off + sizeof(int32_t) * std::max<int64_t>(1, n_logical * pd.num_kv_heads * nl));
   w.total = off;
   return w;
 }
@@ -514,6 +519,21 @@ hipError_t fill_and_upload(rk_tables *t, const WsLayout &ws, void *d_ws, void *s
                   dec_items,
                   dec_comb};
   }
+  {
+    int32_t *ids = reinterpret_cast<int32_t *>(h + ws.pack_ids);
+    t->pack_off.assign(t->num_seqs + 1, 0);
+    int64_t n = 0;
+    for (int32_t b = 0; b < t->num_seqs; ++b) {
+      t->pack_off[b] = n;
+      for (int32_t l = t->layer_begin; l < t->layer_end; ++l)
+        for (int32_t g = 0; g < t->Hkv; ++g) {
+          const int64_t k = t->key(l, g, b);
+          for (int64_t i = t->held_off[k]; i < t->held_off[k + 1]; ++i) ids[n++] = t->held_phys[i];
+        }
+    }
+    t->pack_off[t->num_seqs] = n;
+    t->d_pack_ids = reinterpret_cast<const int32_t *>(dbase + ws.pack_ids);
+  }
   t->d_part_o = t->decode_shaped ? reinterpret_cast<float *>(dbase + ws.part_o) : nullptr;
   t->d_part_lse = t->decode_shaped ? reinterpret_cast<float *>(dbase + ws.part_lse) : nullptr;
   hipStream_t sm = static_cast<hipStream_t>(stream);
@@ -656,6 +676,8 @@ rk::KvWriteParams kv_params(const rk_pool *pool, const rk_tables *t, int32_t lay
   const rk_tables::LayerDev &d = t->dev[layer - t->layer_begin];
   p.k_pages = pool->desc.k_pages;
   p.v_pages = pool->desc.v_pages;
+  p.sink = t->sink;
+  p.window = t->window;
   p.page_base = d.page_base;
   p.page_ids = d.page_ids;
   p.seqs = t->d_seqs;
@@ -1102,6 +1124,80 @@ rk_status rk_seg_key_mass(rk_pool *pool, const rk_tables *t, int32_t layer, cons
   hipError_t e = rk::launch_key_mass(p, pool->desc.head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "key mass kernel launch");
   return RK_OK;
+  RK_GUARD_END
+}
+
+rk_status rk_seg_pack_ledger(const rk_tables *t, int32_t seq, rk_pack_ledger *out) {
+  RK_GUARD_BEGIN
+  if (!t || !out) return fail(RK_ERR_INVALID_ARG, "null tables or out");
+  if (seq < -1 || seq >= t->num_seqs) return fail(RK_ERR_INVALID_ARG, "seq %d outside [-1, %d)", seq, t->num_seqs);
+  rk_pack_ledger L{};
+  const int64_t tok_bytes = 2LL * t->D * t->elem_bytes;
+  for (int32_t b = (seq < 0 ? 0 : seq); b < (seq < 0 ? t->num_seqs : seq + 1); ++b)
+    for (int32_t l = t->layer_begin; l < t->layer_end; ++l)
+      for (int32_t g = 0; g < t->Hkv; ++g) {
+        const int64_t k = t->key(l, g, b);
+        const int cls = t->head_class[(size_t)l * t->Hkv + g];
+        const int64_t np = t->held_off[k + 1] - t->held_off[k];
+        L.pages += np;
+        (cls == RK_GLOBAL ? L.pages_global : L.pages_local) += np;
+        const int64_t Lb = t->kv_len[b];
+        L.dense_tokens += Lb;
+        // held tokens by the rule of the current state: the retained rule once trimmed
+        const int64_t qs = t->trimmed ? Lb : t->q_start[b];
+        int64_t n = Lb;
+        if (cls == RK_LOCAL && Lb > 0) {
+          const int64_t s1 = std::min<int64_t>(t->sink, Lb), w0 = std::max<int64_t>(0, qs - t->window + 1);
+          n = s1 + (Lb - std::max(w0, s1));
+          if (w0 >= Lb) n = s1;
+        }
+        L.tokens += n;
+      }
+  L.packed_bytes = L.pages * 2LL * t->P * t->D * t->elem_bytes;
+  L.token_bytes = L.tokens * tok_bytes;
+  L.dense_bytes = L.dense_tokens * tok_bytes;
+  *out = L;
+  return RK_OK;
+  RK_GUARD_END
+}
+
+namespace {
+rk_status page_copy_impl(rk_pool *pool, const rk_tables *t, int32_t seq, void *buf, size_t buf_bytes, bool pack,
+                         void *stream) {
+  if (!pool || !t || t->pool != pool) return fail(RK_ERR_INVALID_ARG, "null or foreign tables");
+  if (!t->d_ws) return fail(RK_ERR_STATE, "tables were built on the host only (no workspace)");
+  if (t->trimmed) return fail(RK_ERR_STATE, "trimmed tables have no device view; advance them by 0 tokens first");
+  if (seq < -1 || seq >= t->num_seqs) return fail(RK_ERR_INVALID_ARG, "seq %d outside [-1, %d)", seq, t->num_seqs);
+  const int64_t p0 = t->pack_off[seq < 0 ? 0 : seq], p1 = t->pack_off[seq < 0 ? t->num_seqs : seq + 1];
+  const int64_t page_bytes = (int64_t)t->P * t->D * t->elem_bytes;
+  const size_t need = (size_t)((p1 - p0) * 2 * page_bytes);
+  if (pack ? buf_bytes < need : buf_bytes != need)
+    return fail(RK_ERR_INVALID_ARG, "packed buffer has %zu bytes, the held pages take %zu", buf_bytes, need);
+  if (p1 == p0) return RK_OK;
+  if (!buf || !aligned16(buf)) return fail(RK_ERR_INVALID_ARG, "buffer null or not 16-byte aligned");
+  rk::PageCopyParams p{};
+  p.k_pages = pool->desc.k_pages;
+  p.v_pages = pool->desc.v_pages;
+  p.ids = t->d_pack_ids + p0;
+  p.n = p1 - p0;
+  p.buf = buf;
+  p.page_bytes = page_bytes;
+  hipError_t e = rk::launch_page_copy(p, pack, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "page copy launch");
+  return RK_OK;
+}
+}  // namespace
+
+rk_status rk_seg_pack_pages(rk_pool *pool, const rk_tables *t, int32_t seq, void *dst, size_t dst_bytes, void *stream) {
+  RK_GUARD_BEGIN
+  return page_copy_impl(pool, t, seq, dst, dst_bytes, true, stream);
+  RK_GUARD_END
+}
+
+rk_status rk_seg_unpack_pages(rk_pool *pool, const rk_tables *t, int32_t seq, const void *src, size_t src_bytes,
+                              void *stream) {
+  RK_GUARD_BEGIN
+  return page_copy_impl(pool, t, seq, const_cast<void *>(src), src_bytes, false, stream);
   RK_GUARD_END
 }
 

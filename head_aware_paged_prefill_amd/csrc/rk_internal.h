@@ -90,6 +90,8 @@ struct AttnParams {
 struct KvWriteParams {
   void *k_pages;
   void *v_pages;
+  int32_t sink;    // append: a LOCAL head's slots below its window and above the sink are zeroed
+  int32_t window;
   const int32_t *page_base;
   const int32_t *page_ids;
   const SeqInfo *seqs;
@@ -189,7 +191,18 @@ struct DecodeParams {
   int32_t n_items;
 };
 
+// Page hand-off: copies whole K and V pages between the pool and a packed buffer.
+struct PageCopyParams {
+  void *k_pages;
+  void *v_pages;
+  const int32_t *ids;  // physical pages in packed order
+  int64_t n;           // pages
+  void *buf;           // packed: [n][2][page_bytes]
+  int64_t page_bytes;  // page_size * head_dim * element size (a multiple of 16)
+};
+
 hipError_t launch_attention(const AttnParams &p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_page_copy(const PageCopyParams &p, bool pack, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_key_mass(const MassParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_append(const KvWriteParams &p, int dtype, int head_dim, hipStream_t stream);

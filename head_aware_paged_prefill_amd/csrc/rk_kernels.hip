@@ -1,5 +1,6 @@
 // gfx950 (CDNA4) page-writing kernels of the SegPagedAttention prefill library.
 //
+//  * page_copy<PACK>: copies whole held pages to or from a packed buffer (the page hand-off).
 //  * kv_write<...>: writes token rows into held pages, either the new tokens of the call (the online
 //    KV write of EXECUTE, aiboss88.com section 使い方) or a reused document whose keys are rotated from
 //    their offline to their actual position (page "RedKnot – 小红书研发并开源的长上下文大模型推理引擎"
@@ -112,15 +113,29 @@ __global__ void __launch_bounds__(256) kv_write(KvWriteParams p) {
     }
   }
 
-  // Append into the sequence's last page also clears the slots past kv_len (K rows and V columns),
-  // so that every slot of a held page that attention may load holds a finite value.
-  if (!IMPORT && t_hi == si.kv_len && t_hi < lp * P + P) {
-    const int z0 = t_hi - lp * P;  // first unused slot
+  // Every slot of a held page that attention may load must hold a finite value.  The append into
+  // the sequence's last page clears the slots past kv_len; on a LOCAL head's first written page it
+  // clears the slots below its window and above the sink (tokens no query of this call or a later one
+  // sees), which a page newly taken for a window that moved on would otherwise leave unwritten.
+  if (!IMPORT) {
+    int z0 = 0, z1 = 0;  // slots [z0, z1) to clear
+    if (t_hi == si.kv_len && t_hi < lp * P + P) z0 = t_hi - lp * P, z1 = P;
     T *kz = static_cast<T *>(p.k_pages) + (int64_t)pg * P * D;
-    for (int c = tid; c < (P - z0) * D; c += blockDim.x) kz[(int64_t)z0 * D + c] = from_f<T>(0.f);
-    for (int c = tid; c < (P - z0) * D; c += blockDim.x) {
-      const int d = c / (P - z0), sl = z0 + c % (P - z0);
-      vdst[(int64_t)d * P + sl] = from_f<T>(0.f);
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass == 1) {
+        z0 = z1 = 0;
+        if (p.head_class[g] != RK_GLOBAL) {
+          z0 = max(lp * P, p.sink) - lp * P;
+          z1 = min(t_lo, si.q_start_local - p.window + 1) - lp * P;
+        }
+      }
+      const int nz = z1 - z0;
+      if (nz <= 0) continue;
+      for (int c = tid; c < nz * D; c += blockDim.x) kz[(int64_t)z0 * D + c] = from_f<T>(0.f);
+      for (int c = tid; c < nz * D; c += blockDim.x) {
+        const int d = c / nz, sl = z0 + c % nz;
+        vdst[(int64_t)d * P + sl] = from_f<T>(0.f);
+      }
     }
   }
 
@@ -141,7 +156,41 @@ __global__ void __launch_bounds__(256) kv_write(KvWriteParams p) {
   }
 }
 
+// One workgroup per page: the page's K then V, 16 bytes per thread and step, pool <-> packed buffer.
+template <bool PACK>
+__global__ void __launch_bounds__(256) page_copy(PageCopyParams p) {
+  const int64_t i = blockIdx.x;
+  const int64_t pg = p.ids[i];
+  const int64_t nv = p.page_bytes / 16;
+  char *kp = static_cast<char *>(p.k_pages) + pg * p.page_bytes;
+  char *vp = static_cast<char *>(p.v_pages) + pg * p.page_bytes;
+  char *bk = static_cast<char *>(p.buf) + 2 * i * p.page_bytes;
+  char *bv = bk + p.page_bytes;
+  for (int64_t c = threadIdx.x; c < nv; c += blockDim.x) {
+    if (PACK) {
+      const u32x4 a = reinterpret_cast<const u32x4 *>(kp)[c];
+      const u32x4 b = reinterpret_cast<const u32x4 *>(vp)[c];
+      reinterpret_cast<u32x4 *>(bk)[c] = a;
+      reinterpret_cast<u32x4 *>(bv)[c] = b;
+    } else {
+      const u32x4 a = reinterpret_cast<const u32x4 *>(bk)[c];
+      const u32x4 b = reinterpret_cast<const u32x4 *>(bv)[c];
+      reinterpret_cast<u32x4 *>(kp)[c] = a;
+      reinterpret_cast<u32x4 *>(vp)[c] = b;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_page_copy(const PageCopyParams &p, bool pack, hipStream_t stream) {
+  if (p.n <= 0) return hipSuccess;
+  if (pack)
+    hipLaunchKernelGGL(page_copy<true>, dim3((unsigned)p.n), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(page_copy<false>, dim3((unsigned)p.n), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 template <bool IMPORT>
 static hipError_t launch_kv(const KvWriteParams &p, int n_blocks, int dtype, int head_dim, hipStream_t stream) {

@@ -33,7 +33,8 @@ EXPORTS = [
     "rk_seg_tables_workspace_bytes", "rk_seg_build_tables", "rk_seg_tables_export", "rk_seg_tables_schedule",
     "rk_seg_tables_mass_schedule", "rk_seg_tables_stats", "rk_seg_tables_trim", "rk_seg_tables_destroy", "rk_seg_reuse_rerotate",
     "rk_seg_append_kv", "rk_seg_attn_prefill", "rk_seg_key_mass", "rk_seg_tables_advance_workspace_bytes",
-    "rk_seg_tables_advance", "rk_seg_tables_decode_schedule", "rk_seg_attn_decode", "rk_status_string",
+    "rk_seg_tables_advance", "rk_seg_tables_decode_schedule", "rk_seg_attn_decode", "rk_seg_pack_ledger",
+    "rk_seg_pack_pages", "rk_seg_unpack_pages", "rk_status_string",
     "rk_last_error", "rk_seg_version",
 ]
 
@@ -62,6 +63,11 @@ class BatchDesc(ctypes.Structure):
 class TablesStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("pages_held", "total_q", "visible_pairs", "visible_pairs_global",
                                               "work_items", "key_tiles", "workspace_bytes")]
+
+
+class PackLedger(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("pages", "pages_global", "pages_local", "packed_bytes", "tokens",
+                                              "token_bytes", "dense_tokens", "dense_bytes")]
 
 
 _lib = None
@@ -98,6 +104,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rk_seg_tables_advance": [VP, VP, P(I32), VP, ctypes.c_size_t, VP],
         "rk_seg_tables_decode_schedule": [VP, I32, P(I32), I64, P(I64), P(I32), I64],
         "rk_seg_attn_decode": [VP, VP, I32, VP, VP, VP, VP, VP, ctypes.c_float, VP],
+        "rk_seg_pack_ledger": [VP, I32, P(PackLedger)],
+        "rk_seg_pack_pages": [VP, VP, I32, VP, ctypes.c_size_t, VP],
+        "rk_seg_unpack_pages": [VP, VP, I32, VP, ctypes.c_size_t, VP],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -404,6 +413,28 @@ def rk_seg_attn_decode(tables: Tables, layer: int, q, k_new, v_new, o, lse=None,
     [total_q][H][D] bf16 (one row per sequence with a query); lse: [H][total_q] fp32."""
     _check(load().rk_seg_attn_decode(tables.pool.handle, tables.handle, layer, _ptr(q), _ptr(k_new), _ptr(v_new),
                                      _ptr(o), _ptr(lse), float(softmax_scale), _stream(stream)))
+
+
+def rk_seg_pack_ledger(tables: Tables, seq: int = -1) -> dict:
+    """Byte ledger of sequence `seq` (-1: all) of the tables' current state."""
+    out = PackLedger()
+    _check(load().rk_seg_pack_ledger(tables.handle, seq, ctypes.byref(out)))
+    return {f: int(getattr(out, f)) for f, _ in PackLedger._fields_}
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def rk_seg_pack_pages(tables: Tables, seq: int, dst, stream=None) -> None:
+    """Copy the held pages of `seq` (-1: all) into the device tensor dst (>= the ledger's packed_bytes)."""
+    _check(load().rk_seg_pack_pages(tables.pool.handle, tables.handle, seq, _ptr(dst), _nbytes(dst), _stream(stream)))
+
+
+def rk_seg_unpack_pages(tables: Tables, seq: int, src, stream=None) -> None:
+    """Write the packed pages in the device tensor src (exactly the ledger's packed_bytes) into the
+    held pages of `seq` (-1: all) of these tables."""
+    _check(load().rk_seg_unpack_pages(tables.pool.handle, tables.handle, seq, _ptr(src), _nbytes(src), _stream(stream)))
 
 
 def rk_seg_version() -> str:

@@ -141,6 +141,21 @@ typedef struct {
   int64_t workspace_bytes;   /* device workspace the build uses */
 } rk_tables_stats;
 
+/* Byte ledger of the state a tables object holds (rk_seg_pack_ledger): what a hand-off of its pages
+ * moves, against the dense per-head layout that keeps every token of every KV head.  Host, exact
+ * integers; bytes count K and V. */
+typedef struct {
+  int64_t pages;          /* held pages */
+  int64_t pages_global;   /* of GLOBAL heads */
+  int64_t pages_local;    /* of LOCAL heads */
+  int64_t packed_bytes;   /* pages * 2 * page_size * head_dim * element size: what rk_seg_pack_pages moves */
+  int64_t tokens;         /* tokens the held-token rule keeps (the retained rule after trim), summed
+                             over (layer, KV head) */
+  int64_t token_bytes;    /* tokens * 2 * head_dim * element size: the token-granular lower bound */
+  int64_t dense_tokens;   /* kv_len summed over (layer, KV head): every token of every head */
+  int64_t dense_bytes;    /* dense_tokens * 2 * head_dim * element size */
+} rk_pack_ledger;
+
 /* -- pool ---------------------------------------------------------------------------------- */
 
 /* Create a pool over caller-owned page storage.  Host only: no device work.
@@ -315,6 +330,32 @@ rk_status rk_seg_key_mass(rk_pool *pool, const rk_tables *tables, int32_t layer,
 rk_status rk_seg_attn_decode(rk_pool *pool, const rk_tables *tables, int32_t layer, const void *q,
                              const void *k_new, const void *v_new, void *o, float *lse,
                              float softmax_scale, void *stream);
+
+/* -- page hand-off (page "小红书把 KV Cache 按「头」拆了…" (zhichai.net), section 事件内容, and page
+ *    "RedKnot – 小红书研发并开源的长上下文大模型推理引擎" (shshi.cn), section RedKnot核心特点: the
+ *    prefill/decode KV transfer shrinks because only the pages a head keeps are sent) ------------ */
+
+/* Byte ledger of sequence seq (-1: every sequence) of the tables' current state, host only: works on
+ * host-only and trimmed tables.  Errors: RK_ERR_INVALID_ARG. */
+rk_status rk_seg_pack_ledger(const rk_tables *tables, int32_t seq, rk_pack_ledger *out);
+
+/* Copy the held pages of sequence seq (-1: every sequence, in order) into dst: for each sequence,
+ * layer, KV head and held logical page in ascending order, the page's K [page_size][head_dim] then
+ * its V [head_dim][page_size] (the pool's own page layout, so that a receiving pool adopts a page
+ * with one copy), page_size * head_dim elements each.  dst: device, >= the ledger's packed_bytes,
+ * 16-byte aligned, caller-owned.  The tables need a device view: after rk_seg_tables_trim, call
+ * rk_seg_tables_advance with n_new = 0 to get one of the retained state.
+ * Errors: RK_ERR_INVALID_ARG (dst_bytes too small, bad seq), RK_ERR_STATE (no device view), RK_ERR_HIP. */
+rk_status rk_seg_pack_pages(rk_pool *pool, const rk_tables *tables, int32_t seq, void *dst, size_t dst_bytes,
+                            void *stream);
+
+/* The inverse on the receiving side: write the packed pages of src into the held pages of sequence seq
+ * (-1: every sequence) of these tables, in the same order.  The tables must describe the same state
+ * as the sender's (same lengths, classes, sink, window, page size, head dim, layers) -- e.g. built
+ * with q_start = kv_len, whose held pages are the retained state -- so that src_bytes equals their
+ * ledger's packed_bytes (else RK_ERR_INVALID_ARG).  Other errors as rk_seg_pack_pages. */
+rk_status rk_seg_unpack_pages(rk_pool *pool, const rk_tables *tables, int32_t seq, const void *src,
+                              size_t src_bytes, void *stream);
 
 /* -- diagnostics --------------------------------------------------------------------------- */
 

@@ -26,6 +26,16 @@ def _to64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def _poison_free_pages(r):
+    """NaN into every page on the free list, so that a page taken later holds no stale finite data:
+    a kernel that loads a slot nothing wrote then fails the check instead of passing by luck."""
+    free = rk_seg.rk_seg_pool_free_list(r.pool)
+    if free:
+        idx = torch.tensor(free, dtype=torch.long, device="cuda")
+        r.k_pages.index_fill_(0, idx, float("nan"))
+        r.v_pages.index_fill_(0, idx, float("nan"))
+
+
 def decode_parity(wl, steps, what, pattern=None, device_inputs=False, seqs=None):
     """Prefill, trim, then `steps` decode steps.  pattern(step) -> n_new per sequence (default all 1).
     seqs: the sequences whose rows are checked (default all)."""
@@ -43,6 +53,7 @@ def decode_parity(wl, steps, what, pattern=None, device_inputs=False, seqs=None)
         r.import_docs(dinp.docs)
         r.attend(dinp.q, dinp.k_new, dinp.v_new)
         r.trim()
+        _poison_free_pages(r)
         seqs = range(B) if seqs is None else list(seqs)
         hist = {b: [list(reference.head_kv(inp, b, g)) for g in range(Hkv)] for b in seqs}
         kv_class = wl.head_class[wl.layer]
@@ -50,6 +61,7 @@ def decode_parity(wl, steps, what, pattern=None, device_inputs=False, seqs=None)
             n_new = [1] * B if pattern is None else pattern(s)
             active = [b for b in range(B) if n_new[b]]
             r.advance(n_new)
+            _poison_free_pages(r)
             q, k, v = workloads.decode_inputs(wl, s, len(active))
             o, lse = r.decode(q.cuda(), k.cuda(), v.cuda())
             torch.cuda.synchronize()

@@ -32,6 +32,18 @@ def to_dev(inp):
     return dataclasses.replace(inp, q=inp.q.cuda(), k_new=inp.k_new.cuda(), v_new=inp.v_new.cuda(), docs=docs)
 
 
+def cleared_below_window(t, cls, start, kv_len, sink, window, page_size):
+    """Tokens of a LOCAL head's held pages that the append clears to zero: on its first written page
+    (the page of its first query, when the call has queries), those below its window and above its
+    sink -- no query of the call or of a later one sees them, and a page newly taken when the window
+    moved on would otherwise hold unwritten bits there."""
+    t = np.asarray(t)
+    if cls == paging.GLOBAL or kv_len <= start:
+        return np.zeros(len(t), bool)
+    p0 = (start // page_size) * page_size
+    return (t >= max(p0, sink)) & (t < min(start, start - window + 1))
+
+
 def run_call(inp, free_order=None, fill=float("nan")):
     wl = inp.wl
     fo = inp.free_order if free_order is None else free_order
@@ -185,6 +197,10 @@ def test_pages_hold_rerotated_prefix_and_appended_tokens(seed):
             want = paging.pages_of_ranges(paging.held_token_ranges(int(wl.head_class[0, g]), wl.q_starts[b],
                                                                     wl.kv_lens[b], wl.sink, wl.window), wl.page_size)
             assert sorted(set((t // wl.page_size).tolist())) == want
+            z = cleared_below_window(t, int(wl.head_class[0, g]), wl.q_starts[b], wl.kv_lens[b], wl.sink, wl.window,
+                                     wl.page_size)
+            assert (kg[z] == 0).all() and (vg[z] == 0).all(), "slots below a LOCAL window not cleared"
+            kg, vg, t = kg[~z], vg[~z], t[~z]
             kr, vr = k_ref[g, t], v_ref[g, t]
             assert (np.abs(kg - kr) <= bf16_ulp(kr)).all(), "re-rotated keys off by more than one bf16 ulp"
             zero_delta = np.zeros(len(t), bool)

@@ -13,7 +13,7 @@ from head_aware_paged_prefill_amd import rk_seg
 from head_aware_paged_prefill_amd.runner import PrefillRunner
 from oracle import paging, reference, rope
 
-from test_gpu_parity import TOL, bf16_ulp, check, say, to_dev
+from test_gpu_parity import TOL, bf16_ulp, check, cleared_below_window, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -115,6 +115,9 @@ def test_split_pages_hold_recomputed_and_reused_kv(seed):
             want = paging.pages_of_ranges(paging.held_token_ranges(cls, wl.q_starts[b], wl.kv_lens[b], wl.sink,
                                                                     wl.window), wl.page_size)
             assert sorted(set((t // wl.page_size).tolist())) == want
+            z = cleared_below_window(t, cls, start, wl.kv_lens[b], wl.sink, wl.window, wl.page_size)
+            assert (kg[z] == 0).all() and (vg[z] == 0).all(), "slots below a LOCAL window not cleared"
+            kg, vg, t = kg[~z], vg[~z], t[~z]
             new = t >= start
             assert np.array_equal(kg[new], k_ref[t[new]]), "new keys not written bit-exactly"
             assert (np.abs(kg[~new] - exact[t[~new]]) <= bf16_ulp(exact[t[~new]])).all()
