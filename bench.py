@@ -189,6 +189,38 @@ def time_decode(b: "Bench", reps: int) -> dict:
             "dense_bytes": dense_bytes, "items": int(len(items))}
 
 
+def time_pack(b: "Bench", reps: int) -> dict:
+    """Time the page hand-off of the retained state: after the prefill call, trim and advance by 0
+    tokens (a device view of what the pool keeps), rk_seg_pack_pages of every sequence.  The ledger
+    gives the bytes: the held pages' K and V (read once, written once) against the dense per-head
+    layout that keeps every token of every KV head."""
+    wl, r = b.wl, b.r
+    r.build()
+    r.import_docs(b.inp.docs)
+    rk_seg.rk_seg_append_kv(r.tables, wl.layer, b.inp.k_new, b.inp.v_new)
+    rk_seg.rk_seg_attn_prefill(r.tables, wl.layer, b.inp.q, None, None, b.o, b.lse)
+    r.trim()
+    r.advance([0] * wl.num_seqs)
+    led = rk_seg.rk_seg_pack_ledger(r.tables)
+    buf = torch.empty((led["packed_bytes"],), dtype=torch.uint8, device="cuda")
+    rk_seg.rk_seg_pack_pages(r.tables, -1, buf)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rk_seg.rk_seg_pack_pages(r.tables, -1, buf)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    r.release(trim=True)
+    del buf
+    ms = float(np.median(ts))
+    gbs = 2.0 * led["packed_bytes"] / (ms * 1e-3) / 1e9
+    return {"ms": ms, "gbs": gbs, "pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS, "ledger": led,
+            "dense_over_packed": led["dense_bytes"] / max(1, led["packed_bytes"])}
+
+
 def run_workload(wl, steps: int, warmup: int, with_dense: bool):
     log("workload: %s" % wl.name)
     # room for the decode step's new pages (one per (seq, kv head) at most)
@@ -225,6 +257,12 @@ def run_workload(wl, steps: int, warmup: int, with_dense: bool):
             "%.1f MB read of %.1f MB dense (%.2fx fewer)" % (
                 res["decode"]["ms"], res["decode"]["gbs"], res["decode"]["pct_hbm_peak"], res["decode"]["bytes"] / 1e6,
                 res["decode"]["dense_bytes"] / 1e6, res["decode"]["dense_bytes"] / res["decode"]["bytes"]))
+    res["handoff"] = time_pack(b, 10)
+    led = res["handoff"]["ledger"]
+    log("  page hand-off of the retained state: %.1f MB packed (%d pages) vs %.1f MB dense (%.2fx fewer; "
+        "token-exact %.1f MB); pack %.3f ms, %.0f GB/s (%.1f%% of HBM peak)" % (
+            led["packed_bytes"] / 1e6, led["pages"], led["dense_bytes"] / 1e6, res["handoff"]["dense_over_packed"],
+            led["token_bytes"] / 1e6, res["handoff"]["ms"], res["handoff"]["gbs"], res["handoff"]["pct_hbm_peak"]))
     if with_dense:
         wl_d = wl.with_classes(np.ones_like(wl.head_class), wl.name + " all-global")
         bd = Bench(wl_d, dataclasses.replace(inp, wl=wl_d), runner)
