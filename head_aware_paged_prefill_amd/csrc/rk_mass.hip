@@ -187,6 +187,79 @@ __global__ void __launch_bounds__(512, 1) key_mass_bf16(MassParams p) {
     atomicAdd(&sm.acc[(hl ? h1 : h0) * KEYS + KPW * wave + 32 * st + m], tot);
   };
 
+  // Two key sets per wave, every pair of the step visible (the common case: a wave's 64 keys straddle
+  // the causal diagonal or a window edge on a few steps only): a software pipeline over the row
+  // blocks in which every MFMA chain runs beside the weight work of the other chain --
+  //   phase A of block rb: set 1's MFMAs of rb, beside set 0's weights of rb;
+  //   phase B of block rb: set 0's MFMAs of rb + 1, beside set 1's weights of rb --
+  // one MFMA, then a slice of the weights, fenced so that the compiler keeps the order.  The Q
+  // fragments of rb + 1 are loaded into a[c] once the last MFMA reading a[c] is issued, the lse of
+  // rb + 1 into lv[q] once no weight needs lv[q], so that the pipeline takes no extra registers.
+  auto compute_pipe = [&](int buf) {
+    constexpr int EP = 16 / NC;  // weights (of this lane's 16) formed after each MFMA of a chain
+    const bf16_t *Qb = sm.q[buf];
+    const float *l2 = sm.lse2[buf];
+    auto qfrag = [&](int rb, int c) {
+      const int qr = rb * 32 + m;
+      return *reinterpret_cast<const bf16x8 *>(Qb + qr * D + (((2 * c + hl) ^ kswz<D>(qr)) << 3));
+    };
+    auto lvec = [&](int rb, int q4) { return *reinterpret_cast<const f32x4 *>(l2 + rb * 32 + 8 * q4 + 4 * hl); };
+    bf16x8 a[NC];
+    f32x4 lv[4];
+    float lo = 0.f, hi = 0.f;
+    auto piece = [&](const f32x16 &acc, int c) {
+#pragma unroll
+      for (int k = 0; k < EP; ++k) {
+        const int i = c * EP + k;
+        const float w = fast_exp2(fmaf(acc[i], c2, -lv[i / 4][i % 4]));
+        if (i < 8) lo += w;
+        else hi += w;
+      }
+    };
+    auto finish = [&](int rb, int st) {
+      const int h0 = head_of(2 * rb), h1 = head_of(2 * rb + 1);
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+      atomicAdd(&sm.acc[(hl ? h1 : h0) * KEYS + KPW * wave + 32 * st + m], __uint_as_float(r[0]) + __uint_as_float(r[1]));
+      lo = hi = 0.f;
+    };
+#pragma unroll
+    for (int c = 0; c < NC; ++c) a[c] = qfrag(0, c);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) lv[q4] = lvec(0, q4);
+    f32x16 s0 = {}, s1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], kf[0][c], s0, 0, 0, 0);
+    auto block = [&](const int rb) __attribute__((always_inline)) {
+      s1 = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {  // phase A
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], kf[NS - 1][c], s1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        piece(s0, c);
+        if (rb + 1 < NRB) a[c] = qfrag(rb + 1, c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      finish(rb, 0);
+      if (rb + 1 < NRB) {
+        s0 = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {  // phase B
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], kf[0][c], s0, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          piece(s1, c);
+          if ((c * EP + EP) % 4 == 0) lv[(c * EP) / 4] = lvec(rb + 1, (c * EP) / 4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) piece(s1, c);
+      }
+      finish(rb, 1);
+    };
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) block(rb);
+  };
+
   auto compute = [&](int s, int buf) {
     const int ts = start + (k_last - s) * T;
     const int tmax = min(ts + T - 1, t_last);
@@ -200,6 +273,10 @@ __global__ void __launch_bounds__(512, 1) key_mass_bf16(MassParams p) {
       full[st] = kmax <= ts && (global || kmax < SK || kmin > tmax - W);
     }
     if (!any) return;  // no row of the step sees a key of this wave
+    if (NS == 2 && full[0] && full[NS - 1]) {  // the common case: both sets fully visible
+      compute_pipe(buf);
+      return;
+    }
     const bf16_t *Qb = sm.q[buf];
     const float *l2 = sm.lse2[buf];
 #pragma unroll
