@@ -160,7 +160,7 @@ constexpr int kMassChunkSteps = 64;  // steps per query chunk
 // Decode (one query row per sequence): split-KV work items, one wave each, over key ranges of the
 // query's visible set; the partial (o, lse) of item i go to slot i and are merged per (seq, kv head)
 // by the combine kernel.
-constexpr int kDecodeTargetItems = 2048;  // items per layer the key chunk aims at (8 waves per CU)
+constexpr int kDecodeTargetItems = 4096;  // items per layer the key chunk aims at (two rounds of 8 waves per CU)
 constexpr int kDecodeMinChunk = 256;      // keys
 struct DecItem {
   int32_t seq;

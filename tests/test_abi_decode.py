@@ -137,15 +137,15 @@ def test_decode_items_cover_the_visible_keys_once(seed):
             assert (cover == vis.astype(np.int64)).all(), "items must cover each visible key exactly once"
             ks = mine[:, 2:].tolist()
             assert ks == sorted(ks)
-    # one key chunk, aiming the layer at 2048 items: a multiple of 32, at least 256; no item crosses
+    # one key chunk, aiming the layer at 4096 items: a multiple of 32, at least 256; no item crosses
     # a multiple of it
     keys = sum(int(attention.visibility_mask(int(c["hc"][0, g]), np.array([L - 1]), L, c["S"], c["W"]).sum())
                for b, L in enumerate(c["kv"]) if n_new[b] for g in range(Hkv))
     ranges = sum(len(_ranges(int(c["hc"][0, g]), L, c["S"], c["W"])) for b, L in enumerate(c["kv"]) if n_new[b]
                  for g in range(Hkv))
-    room = max(2048 // 4, 2048 - 2 * ranges)
+    room = max(4096 // 4, 4096 - 2 * ranges)
     chunk = max(256, -(-(-(-keys // room)) // 32) * 32)
-    assert len(items) <= 2048 or room == 2048 // 4
+    assert len(items) <= 4096 or room == 4096 // 4
     for _, _, k0, k1 in items.tolist():
         assert k0 // chunk == (k1 - 1) // chunk
     rk_seg.rk_seg_tables_destroy(t)
