@@ -35,7 +35,7 @@ def _run(cmd, verbose):
     return r
 
 
-HOST_SOURCES = ["rk_host.cpp", "rk_sched.cpp"]
+HOST_SOURCES = ["rk_host.cpp", "rk_sched.cpp", "rk_sched_ops.cpp"]
 HIP_SOURCES = ["rk_attn.hip", "rk_kernels.hip", "rk_mass.hip", "rk_decode.hip"]
 
 

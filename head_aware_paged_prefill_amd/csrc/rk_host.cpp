@@ -23,7 +23,9 @@
 #include <vector>
 
 #include "rk_internal.h"
+#include "rk_ops.h"
 #include "rk_sched.h"
+#include "rk_sched_ops.h"
 #include "rk_seg.h"
 
 namespace {

@@ -21,7 +21,7 @@
 #include <stdint.h>
 
 #include "rk_device.h"
-#include "rk_internal.h"
+#include "rk_ops.h"
 #include "rk_seg.h"
 
 #include <algorithm>
