@@ -332,6 +332,52 @@ def cpu_baseline(wl, budget_s: float = 15.0):
                       "dense masked attention), useful flops only" % (blocks, t_used)}
 
 
+def cpu_next_baselines(wl, budget_s: float = 4.0):
+    """The fp64 oracle beside the decode, per-key mass and hand-off kernels, each on a bounded sample of the
+    workload on the host cores, in the units the GPU figures use."""
+    from oracle import attention as oatt
+    from oracle import decode as odec
+    rng = np.random.Generator(np.random.PCG64(7))
+    D, Hkv, G = wl.head_dim, wl.num_kv_heads, wl.group
+    cls = wl.head_class[wl.layer]
+    out = {}
+    # decode: one sequence's row (all heads) over a random K/V history one token longer than the prefill
+    L = wl.kv_lens[0] + 1
+    k = [rng.standard_normal((L, D)) for _ in range(Hkv)]
+    v = [rng.standard_normal((L, D)) for _ in range(Hkv)]
+    n, t_used, nbytes = 0, 0.0, 0
+    vis = sum(int(oatt.visibility_mask(int(cls[g]), np.array([L - 1]), L, wl.sink, wl.window).sum()) for g in range(Hkv))
+    while t_used < budget_s and n < 64:
+        q = rng.standard_normal((wl.num_q_heads, D))
+        t0 = time.perf_counter()
+        odec.decode_step(q, k, v, cls, wl.sink, wl.window)
+        t_used += time.perf_counter() - t0
+        n += 1
+        nbytes += vis * 2 * D * 2
+    out["decode"] = {"value": nbytes / t_used / 1e9, "unit": "GB/s (algorithmic K/V bytes at 2 bytes per element)",
+                     "kind": "oracle", "sample": "%d decode rows of one %d-token sequence, all %d q heads (%.1f s)" % (
+                         n, L, wl.num_q_heads, t_used)}
+    del k, v
+    # per-key mass: 256-row blocks of (sequence, q head) over the visible keys, column sums of the weights
+    n, t_used, flops = 0, 0.0, 0.0
+    Lm = wl.kv_lens[0]
+    km = rng.standard_normal((Lm, D))
+    while t_used < budget_s and n < 256:
+        g = int(rng.integers(0, Hkv))
+        r0 = int(rng.integers(0, max(1, (Lm - wl.q_starts[0]) // 256))) * 256 + wl.q_starts[0]
+        pos = np.arange(r0, min(Lm, r0 + 256))
+        q = rng.standard_normal((len(pos), D))
+        t0 = time.perf_counter()
+        mask = oatt.visibility_mask(int(cls[g]), pos, Lm, wl.sink, wl.window)
+        oatt.softmax_rows(q, km, mask, 1.0 / np.sqrt(D)).sum(axis=0)
+        t_used += time.perf_counter() - t0
+        flops += 2.0 * D * float(mask.sum())
+        n += 1
+    out["key_mass"] = {"value": flops / t_used / 1e12, "unit": "TFLOP/s (QK half, 2 D per visible pair)",
+                       "kind": "oracle", "sample": "%d random 256-row blocks (%.1f s)" % (n, t_used)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +416,10 @@ def main():
         extra["dsv4flash_execute_split_128k"] = run_workload(workloads.dsv4flash_split(3), max(2, a.steps // 2), 1,
                                                              with_dense=True)
     cpu = None if a.no_cpu else cpu_baseline(wl, a.cpu_seconds)
+    if cpu is not None:
+        main_res["cpu_oracle_beside"] = cpu_next_baselines(wl)
+        log("  oracle on the host: decode %.2f GB/s, per-key mass %.4f TFLOP/s" % (
+            main_res["cpu_oracle_beside"]["decode"]["value"], main_res["cpu_oracle_beside"]["key_mass"]["value"]))
     ms_attn = main_res["ms_attention"]
     achieved = main_res["tflops_attention"]
     line = {

@@ -122,6 +122,14 @@ def test_decode_long_context_splits_and_combines():
     decode_parity(wl, 4, wl.name)
 
 
+@pytest.mark.parametrize("G,D,P", [(16, 64, 16), (8, 64, 256), (2, 128, 128)])
+def test_decode_shapes(G, D, P):
+    wl = workloads.random_small(4, torch.bfloat16)
+    wl = dataclasses.replace(wl, num_q_heads=G * wl.num_kv_heads, head_dim=D, page_size=P,
+                             name="decode G=%d D=%d P=%d" % (G, D, P))
+    decode_parity(wl, 6, wl.name)
+
+
 def test_decode_page_64():
     wl = workloads.random_small(3, torch.bfloat16)
     wl = dataclasses.replace(wl, page_size=64, head_dim=128, kv_lens=[700, 1300], q_starts=[0, 650], doc_len=200,

@@ -163,3 +163,28 @@ def test_pack_needs_a_device_view():
         assert ei.value.status == rk_seg.RK_ERR_STATE
     finally:
         r.close()
+
+
+def test_pack_roundtrip_fp32_pool_bit_exact():
+    # the hand-off moves bytes: an fp32 pool packs and unpacks bit for bit as well
+    wl = workloads.random_small(6, torch.float32, allow_reuse=False)
+    say("pack fp32 %s: kv_lens=%s P=%d" % (wl.name, wl.kv_lens, wl.page_size))
+    inp, ra = _prefill_retained(wl, workloads.pool_pages_needed_hint(wl) + wl.pool_slack)
+    order_b = np.random.Generator(np.random.PCG64(91)).permutation(len(inp.free_order) + 5).astype(np.int32)
+    rb = PrefillRunner(wl, free_order=order_b, poison=True)
+    try:
+        led = rk_seg.rk_seg_pack_ledger(ra.tables)
+        buf = torch.empty((led["packed_bytes"],), dtype=torch.uint8, device="cuda")
+        rk_seg.rk_seg_pack_pages(ra.tables, -1, buf)
+        torch.cuda.synchronize()
+        assert torch.equal(buf, _packed_from_pool(ra, _replay_ids(wl, inp)))
+        rb.tables = rk_seg.rk_seg_build_tables(rb.pool, wl.layer, wl.layer + 1, wl.num_q_heads, wl.kv_lens, wl.kv_lens,
+                                               wl.head_class, wl.sink, wl.window, device=True)
+        rk_seg.rk_seg_unpack_pages(rb.tables, -1, buf)
+        back = torch.empty_like(buf)
+        rk_seg.rk_seg_pack_pages(rb.tables, -1, back)
+        torch.cuda.synchronize()
+        assert torch.equal(back, buf)
+    finally:
+        ra.close()
+        rb.close()
