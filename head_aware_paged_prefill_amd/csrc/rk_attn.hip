@@ -18,9 +18,12 @@
 //    exactly its registers 8c..8c+7, converted to bf16 in place -- no shuffles.
 //  * V pages are stored channel-major ([D][P]) so the A operand of PV (8 consecutive keys of one
 //    channel) is one 16-byte LDS read.
-//  * Tiles reach LDS by direct global->LDS 16-byte loads (scalar page address + 32-bit lane
-//    offset), one 1 KB block per instruction; XOR swizzles of the 16-byte chunks keep the operand
-//    reads free of bank conflicts.
+//  * Tiles reach LDS by direct 16-byte buffer->LDS loads (a descriptor on the page's scalar address,
+//    32-bit lane offset), one 1 KB block per instruction; XOR swizzles of the 16-byte chunks keep the
+//    operand reads free of bank conflicts.  The buffer form matters: with the global form in flight
+//    the compiler makes every LDS operand read wait for all outstanding ones.
+//  * Operand reads run one MFMA group ahead of their products (K chunk c + 1 during chunk c, V of
+//    the first PV group during the softmax), held in place by sched_barrier(0).
 //  * Two 64-key tiles per step, double-buffered: the next step's loads are issued before this
 //    step's MFMA work; one barrier per step.  The buffer index is a compile-time constant (the step
 //    loop is unrolled by two), so operand addresses are lane registers plus immediate offsets.
@@ -109,6 +112,7 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
   const int Pt = P < BN ? P : BN;
   const int n_logical = (L + P - 1) >> log2P;
   const int64_t page_elems = (int64_t)P * D;
+  const uint32_t page_bytes = (uint32_t)page_elems * 2;
   // Pages a tile touches but the head does not hold (or past the sequence's last page) are read
   // from this page instead: the page of the item's last query, held and fully written (the append
   // clears its slots past kv_len).  Its keys are masked out, so only finiteness matters.
@@ -206,7 +210,7 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
       } else {
         const int pg = fix(__builtin_amdgcn_readlane(ids, lane0 + (P < BN ? (k_key0[u] >> log2P) : 0)));
         const char *page = reinterpret_cast<const char *>(kpg + (int64_t)pg * page_elems + ko);  // uniform
-        load_lds16(page + opaque(k_loff[u]), &sm.k[buf][x][b * 512]);
+        load_lds16_buf(page, k_loff[u], page_bytes, &sm.k[buf][x][b * 512]);
       }
       const int vo = P > BN ? (j0 & (P - 1)) : 0;
       if constexpr (v_split) {
@@ -215,7 +219,7 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
       } else {
         const int pg = fix(__builtin_amdgcn_readlane(ids, lane0 + v_pi[u]));
         const char *page = reinterpret_cast<const char *>(vpg + (int64_t)pg * page_elems + vo);  // uniform
-        load_lds16(page + opaque(v_loff[u]), &sm.v[buf][x][b * 512]);
+        load_lds16_buf(page, v_loff[u], page_bytes, &sm.v[buf][x][b * 512]);
       }
     }
   };
@@ -240,13 +244,29 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
     if (skip) return;
     // S^T for the tile's 64 keys (two 32-key blocks) x this wave's 32 queries
     f32x16 s[2] = {};
+    {
+      bf16x8 ka[2][2];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+      for (int kb = 0; kb < 2; ++kb) ka[0][kb] = *reinterpret_cast<const bf16x8 *>(Kb + k_rd[0] + 32 * kb * D);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + k_rd[c] + 32 * kb * D);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+      for (int c = 0; c < NC; ++c) {
+        const int cur = c & 1;
+        if (c + 1 < NC) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            ka[cur ^ 1][kb] = *reinterpret_cast<const bf16x8 *>(Kb + k_rd[c + 1] + 32 * kb * D);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][kb], qf[c], s[kb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    // V operands of the first PV group, read while the softmax runs
+    bf16x8 va[2][ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) va[0][db] = *reinterpret_cast<const bf16x8 *>(Vb + v_rd[0] + db * 32 * BN);
+    __builtin_amdgcn_sched_barrier(0);
     if (!full) {
       // key of register i of block kb: jb + 16 * (i / 8) + i % 8, jb = j0 + 32 kb + 8 hl
 #pragma unroll
@@ -305,14 +325,19 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
     lsum += ps;
     // O^T += V^T P^T
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int cur = g4 & 1;
+      if (g4 + 1 < 4) {
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+        for (int db = 0; db < ND; ++db)
+          va[cur ^ 1][db] = *reinterpret_cast<const bf16x8 *>(Vb + v_rd[g4 + 1] + db * 32 * BN);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Vb + v_rd[2 * kb + cc] + db * 32 * BN);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kb][cc], oacc[db], 0, 0, 0);
-        }
+      for (int db = 0; db < ND; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cur][db], pk[g4 >> 1][g4 & 1], oacc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // Loads retire in issue order.  Order per step: data of the next step, then the page ids of the

@@ -66,6 +66,16 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   return x;
 }
 
+// 16 bytes per lane from a wave-uniform base plus a 32-bit lane offset into a dense 1 KB LDS block,
+// in the buffer form (a raw descriptor whose range is `bytes`; offsets past it read zeros).  The
+// compiler's wait insertion treats an LDS load in the global form as an LDS access of unknown order,
+// so while one is in flight every later LDS read waits for all of them (lgkmcnt(0)); in the buffer
+// form the LDS operand reads keep their partial waits and can run ahead of the products using them.
+__device__ __forceinline__ void load_lds16_buf(const void *base, uint32_t voff, uint32_t bytes, void *lds_block) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_block, 16, voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_block) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
                                    (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
