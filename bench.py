@@ -186,7 +186,7 @@ def time_decode(b: "Bench", reps: int) -> dict:
     ms = float(np.median(ts))
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"ms": ms, "gbs": gbs, "pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS, "bytes": nbytes,
-            "dense_bytes": dense_bytes, "items": int(len(items))}
+            "dense_bytes": dense_bytes, "items": int((items[:, 3] > items[:, 2]).sum())}
 
 
 def time_pack(b: "Bench", reps: int) -> dict:

@@ -4,12 +4,14 @@
 // 「头」拆了…" (zhichai.net), section 事件内容: GLOBAL heads read every context page, LOCAL heads only
 // their sink and recent-window pages).
 //
-//  * decode_bf16<D>: one wave per split-KV item (seq, kv head, key range).  The G <= 16 query rows of
-//    the KV head are the N = 16 columns of v_mfma_f32_16x16x32_bf16: S^T = K Q^T with keys as M, then
-//    O^T += V^T P^T with channels as M, so P never leaves registers (the two 16-key halves of a 32-key
-//    tile give each lane the 8 keys its B operand needs, in the order the V loads follow).  K and V
-//    come straight from the pages into registers (16- and 8-byte loads off a scalar page base), one
-//    32-key tile ahead.  Online softmax in fp32; the item writes its normalised partial output and lse.
+//  * decode_bf16<D>: one wave per split-KV item (seq, kv head, key range), kDecodeWaves waves per
+//    workgroup on consecutive items of one (seq, kv head).  The G <= 16 query rows of the KV head are
+//    the N = 16 columns of v_mfma_f32_16x16x32_bf16: S^T = K Q^T with keys as M, then O^T += V^T P^T
+//    with channels as M, so P never leaves registers (the two 16-key halves of a 32-key tile give each
+//    lane the 8 keys its B operand needs, in the order the V loads follow).  K and V come straight
+//    from the pages into registers (16- and 8-byte loads off a scalar page base), one 32-key tile
+//    ahead.  Online softmax in fp32.  The waves merge their (max, sum, unnormalised o) in LDS, and the
+//    workgroup writes one normalised partial output and lse.
 //  * decode_combine<D>: merges the partials of each query row: lse = log sum_s e^{lse_s},
 //    o = sum_s e^{lse_s - lse} o_s (the split-KV combine), one workgroup per row.
 // Decode reads every visible K/V byte once, so it is bound by HBM bandwidth, not by the MFMAs.
@@ -48,11 +50,15 @@ struct DecTile {
 };
 
 template <int D>
-__global__ void __launch_bounds__(64) decode_bf16(DecodeParams p) {
+__global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p) {
   constexpr int KS = D / 32;  // 32-channel steps of QK
   constexpr int DT = D / 16;  // 16-channel tiles of PV
-  const int lane = threadIdx.x, c16 = lane & 15, q4 = lane >> 4;
-  const DecItem it = p.items[blockIdx.x];
+  constexpr int NW = kDecodeWaves;
+  __shared__ f32x4 sm_o[NW][16][D / 4];  // per wave: unnormalised O^T columns (query rows)
+  __shared__ float sm_m[NW][16], sm_l[NW][16];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, c16 = lane & 15, q4 = lane >> 4;
+  const DecItem it = p.items[blockIdx.x * NW + wave];
   const int b = it.seq, g = it.kv_head, k0 = it.k0, k1 = it.k1;
   const SeqInfo si = p.seqs[b];
   const int L = si.kv_len, P = p.P, G = p.G;
@@ -155,10 +161,10 @@ __global__ void __launch_bounds__(64) decode_bf16(DecodeParams p) {
   // tile t's loads are issued while tile t - 1 is computed; its page ids were looked up two tiles
   // earlier (scalar loads stay in flight: no LDS instruction shares their wait counter)
   const int t0 = k0 & ~31;
-  const int ntiles = ((k1 - 1 - t0) >> 5) + 1;
+  const int ntiles = k1 > k0 ? ((k1 - 1 - t0) >> 5) + 1 : 0;  // a padding item has no keys
   DecTile<D> buf[2];
   Pages pn = pages_of(t0), pn2 = pages_of(t0 + 32);
-  load(t0, pn, buf[0]);
+  if (ntiles > 0) load(t0, pn, buf[0]);
   pn = pn2;
   pn2 = pages_of(t0 + 64);
   for (int t = 0; t < ntiles; t += 2) {
@@ -174,31 +180,60 @@ __global__ void __launch_bounds__(64) decode_bf16(DecodeParams p) {
     }
   }
 
-  // row sum over the four lane groups; normalised partial output and lse (natural log)
+  // row sum over the four lane groups; the wave's (max, sum, unnormalised o) of each query row to LDS
+  // (a padding item: max -inf, sum 0, o 0)
   l = groups_sum(l);
-  if (c16 < G) {
-    const float inv = 1.0f / l;
-    float *po = p.part_o + ((int64_t)blockIdx.x * G + c16) * D + 4 * q4;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt) = o[dt] * inv;
-    if (q4 == 0) p.part_lse[(int64_t)blockIdx.x * G + c16] = (m + __log2f(l)) * 0.6931471805599453f;
+  for (int dt = 0; dt < DT; ++dt) sm_o[wave][c16][4 * dt + q4] = o[dt];
+  if (q4 == 0) {
+    sm_m[wave][c16] = m;
+    sm_l[wave][c16] = l;
+  }
+  __syncthreads();
+  // merge: thread (row r, channel quarter-group cq) combines the waves' parts of row r
+  constexpr int CPT = D / 64;  // f32x4 chunks per thread: 16 rows x 16 threads cover [16][D / 4]
+  const int r = threadIdx.x >> 4, cq = threadIdx.x & 15;
+  if (r < G) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][r]);
+    float a[NW], tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      a[w] = sm_m[w][r] == -INFINITY ? 0.f : fast_exp2(sm_m[w][r] - mx);
+      tot += a[w] * sm_l[w][r];
+    }
+    const float inv = 1.0f / tot;
+    float *po = p.part_o + ((int64_t)blockIdx.x * G + r) * D;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c4 = cq + 16 * j;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc += a[w] * sm_o[w][r][c4];
+      *reinterpret_cast<f32x4 *>(po + 4 * c4) = acc * inv;
+    }
+    if (cq == 0) p.part_lse[(int64_t)blockIdx.x * G + r] = (mx + __log2f(tot)) * 0.6931471805599453f;
   }
 }
 
 // One workgroup per query row (seq, q head): lse = max + log sum_s e^{lse_s - max} and
 // o = sum_s e^{lse_s - lse} o_s over the row's partials s.  The partials are spread over NG groups
-// of D / 4 threads (each thread four channels), which are summed through LDS at the end.
+// of D / 4 threads (each thread four channels), which are summed through LDS at the end; a thread
+// keeps U partial loads in flight (the combine of a long GLOBAL head is latency-bound otherwise).
 template <int D>
 __global__ void __launch_bounds__(256) decode_combine(DecodeParams p) {
   constexpr int TPG = D / 4;         // threads per group: one 16-byte chunk of a partial each
   constexpr int NG = 256 / TPG;      // groups
+  constexpr int U = 8;               // partials in flight per thread
   __shared__ float red[256];
   __shared__ f32x4 part[NG][TPG];
   const int tid = threadIdx.x;
   const int G = p.G;
   const int bg = blockIdx.x / G, r = blockIdx.x - bg * G;
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
-  const int s0 = p.comb_off[bg], s1 = p.comb_off[bg + 1];
+  // the row's partial slots: one per workgroup of kDecodeWaves items
+  const int s0 = p.comb_off[bg] / kDecodeWaves, s1 = p.comb_off[bg + 1] / kDecodeWaves;
   if (s0 == s1) return;  // the sequence has no query row
   const SeqInfo si = p.seqs[b];
   auto block_reduce = [&](float v, bool is_max) {
@@ -221,10 +256,17 @@ __global__ void __launch_bounds__(256) decode_combine(DecodeParams p) {
   const float lse = mx + logf(tot);
   const int grp = tid / TPG, d4 = tid - grp * TPG;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = s0 + grp; s < s1; s += NG) {
-    const float w = expf(p.part_lse[(int64_t)s * G + r] - lse);
-    acc += w * *reinterpret_cast<const f32x4 *>(p.part_o + ((int64_t)s * G + r) * D + 4 * d4);
+  for (int s = s0 + grp; s < s1; s += NG * U) {
+    f32x4 v[U];
+    float l[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int su = min(s + NG * u, s1 - 1);  // past the row's last partial: reloaded, weight 0
+      v[u] = *reinterpret_cast<const f32x4 *>(p.part_o + ((int64_t)su * G + r) * D + 4 * d4);
+      l[u] = p.part_lse[(int64_t)su * G + r];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += (s + NG * u < s1 ? expf(l[u] - lse) : 0.f) * v[u];
   }
   part[grp][d4] = acc;
   __syncthreads();
@@ -240,12 +282,13 @@ __global__ void __launch_bounds__(256) decode_combine(DecodeParams p) {
 
 hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t stream) {
   if (p.n_items <= 0) return hipSuccess;
-  const dim3 grid((unsigned)p.n_items), comb((unsigned)(p.num_seqs * p.Hkv * p.G));
+  if (p.n_items % kDecodeWaves) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.n_items / kDecodeWaves)), comb((unsigned)(p.num_seqs * p.Hkv * p.G));
   if (head_dim == 128) {
-    hipLaunchKernelGGL(decode_bf16<128>, grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_bf16<128>, grid, dim3(64 * kDecodeWaves), 0, stream, p);
     hipLaunchKernelGGL(decode_combine<128>, comb, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(decode_bf16<64>, grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_bf16<64>, grid, dim3(64 * kDecodeWaves), 0, stream, p);
     hipLaunchKernelGGL(decode_combine<64>, comb, dim3(256), 0, stream, p);
   }
   return hipGetLastError();

@@ -295,10 +295,11 @@ WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, CallSched *sched)
     }
   }
   if (decode) {
+    const int64_t slots = ceil_div(dec_bound, rk::kDecodeWaves);  // one partial per workgroup
     w.part_o = off;
-    off = align_up(off + sizeof(float) * dec_bound * G * pd.head_dim);
+    off = align_up(off + sizeof(float) * slots * G * pd.head_dim);
     w.part_lse = off;
-    off = align_up(off + sizeof(float) * dec_bound * G);
+    off = align_up(off + sizeof(float) * slots * G);
   }
   w.pack_ids = off;  // at most every logical page of every (layer, kv head, seq)
   off = align_up(off + sizeof(int32_t) * std::max<int64_t>(1, n_logical * pd.num_kv_heads * nl));

@@ -80,10 +80,12 @@ constexpr int kMassRun = 16;         // units placed together on one XCD
 constexpr int kMassChunkSteps = 64;  // steps per query chunk
 
 // Decode (one query row per sequence): split-KV work items, one wave each, over key ranges of the
-// query's visible set; the partial (o, lse) of item i go to slot i and are merged per (seq, kv head)
-// by the combine kernel.
-constexpr int kDecodeTargetItems = 4096;  // items per layer the key chunk aims at (two rounds of 8 waves per CU)
-constexpr int kDecodeMinChunk = 256;      // keys
+// query's visible set.  kDecodeWaves consecutive items belong to one (seq, kv head) (padding items
+// have an empty range) and form one workgroup, which merges their partials in LDS into slot
+// item / kDecodeWaves; the combine kernel merges the slots of each (seq, kv head).
+constexpr int kDecodeWaves = 4;           // items (waves) per workgroup
+constexpr int kDecodeTargetItems = 8192;  // items per layer the key chunk aims at (eight waves per SIMD)
+constexpr int kDecodeMinChunk = 128;      // keys
 struct DecItem {
   int32_t seq;
   int32_t kv_head;
@@ -98,10 +100,10 @@ struct DecodeParams {
   const int32_t *page_base;
   const int32_t *page_ids;
   const SeqInfo *seqs;
-  const DecItem *items;   // slot order: grouped by (seq, kv head), ranges ascending
-  const int32_t *comb_off;  // [num_seqs * Hkv + 1]: first slot of (seq, kv head) = b * Hkv + g
-  float *part_o;          // [n_items][G][D] fp32, normalised partial outputs
-  float *part_lse;        // [n_items][G] fp32, natural log
+  const DecItem *items;   // grouped by (seq, kv head), ranges ascending, kDecodeWaves per workgroup
+  const int32_t *comb_off;  // [num_seqs * Hkv + 1]: first item of (seq, kv head) = b * Hkv + g
+  float *part_o;          // [n_items / kDecodeWaves][G][D] fp32, normalised partial outputs
+  float *part_lse;        // [n_items / kDecodeWaves][G] fp32, natural log
   int32_t num_seqs;
   int32_t H;
   int32_t Hkv;
@@ -110,7 +112,7 @@ struct DecodeParams {
   int32_t log2P;
   float scale_log2;
   int32_t total_q;
-  int32_t n_items;
+  int32_t n_items;  // a multiple of kDecodeWaves
 };
 
 // Page hand-off: copies whole K and V pages between the pool and a packed buffer.

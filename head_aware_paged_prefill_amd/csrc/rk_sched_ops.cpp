@@ -90,8 +90,10 @@ int decode_ranges(int cls, int32_t L, int32_t S, int32_t W, int32_t r[4]) {
 }  // namespace
 
 // A range of n keys cut at multiples of the chunk gives at most n / chunk + 2 items, and keys / chunk
-// <= kDecodeTargetItems; a (seq, kv head) has at most two ranges.
-int64_t decode_items_bound(const SchedInput &t) { return kDecodeTargetItems + 4 * (int64_t)t.num_seqs * t.Hkv; }
+// <= kDecodeTargetItems; a (seq, kv head) has at most two ranges and kDecodeWaves - 1 padding items.
+int64_t decode_items_bound(const SchedInput &t) {
+  return kDecodeTargetItems + (4 + kDecodeWaves - 1) * (int64_t)t.num_seqs * t.Hkv;
+}
 
 void decode_schedule(const SchedInput &t, std::vector<DecItem> &items, std::vector<int32_t> &comb_off) {
   items.clear();
@@ -120,6 +122,7 @@ void decode_schedule(const SchedInput &t, std::vector<DecItem> &items, std::vect
         for (int64_t c = r[2 * i] / chunk; c * chunk < r[2 * i + 1]; ++c)
           items.push_back({b, g, (int32_t)std::max<int64_t>(r[2 * i], c * chunk),
                            (int32_t)std::min<int64_t>(r[2 * i + 1], (c + 1) * chunk)});
+      while (items.size() % kDecodeWaves) items.push_back({b, g, 0, 0});  // workgroup of one (seq, kv head)
     }
   comb_off[(size_t)t.num_seqs * t.Hkv] = (int32_t)items.size();
 }

@@ -26,12 +26,13 @@ int64_t mass_units_bound(const SchedInput &in, int32_t keys, int32_t tokens);
 // [max(0, L - W), L), merged when they touch).  A range is cut at multiples of the key chunk, which
 // keeps the layer within kDecodeTargetItems items, two per range reserved for the cuts that do not
 // fall on a range boundary (at least kDecodeMinChunk keys, a multiple of 32).
-// Items come grouped by (seq, kv head) in ascending key order; comb_off[b * Hkv + g] is the first
-// item of (b, g) and comb_off[num_seqs * Hkv] the item count.
+// Items come grouped by (seq, kv head) in ascending key order, each group padded with empty items
+// (k0 = k1 = 0) to a multiple of kDecodeWaves; comb_off[b * Hkv + g] is the first item of (b, g) and
+// comb_off[num_seqs * Hkv] the item count.
 void decode_schedule(const SchedInput &in, std::vector<DecItem> &items, std::vector<int32_t> &comb_off);
 
 // An upper bound of decode_schedule's item count for any head classes: kDecodeTargetItems plus four
-// per (seq, kv head).
+// cut items and kDecodeWaves - 1 padding items per (seq, kv head).
 int64_t decode_items_bound(const SchedInput &in);
 
 }  // namespace rk

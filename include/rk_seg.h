@@ -243,11 +243,12 @@ rk_status rk_seg_tables_mass_schedule(const rk_tables *tables, int32_t layer, in
  * [cap][4] = (seq, kv_head, k0, k1): the keys [k0, k1) of the sequence, all visible to its query
  * (the token at kv_len - 1).  A (seq, kv head)'s visible keys are GLOBAL [0, kv_len) or LOCAL
  * [0, min(sink, kv_len)) and [max(0, kv_len - window), kv_len) (merged when they touch), cut at
- * multiples of one key chunk (a multiple of 32, at least 256).  Items come grouped by (seq, kv
- * head), ascending; comb_off [comb_cap] receives the first item of (seq b, kv head g) at
- * b * num_kv_heads + g and the item count at num_seqs * num_kv_heads.  *n_items = 0 when the tables
- * are not decode-shaped (a sequence with more than one query row, or more than 16 q heads per KV
- * head).  Any output pointer may be NULL. */
+ * multiples of one key chunk (a multiple of 32, at least 128).  Items come grouped by (seq, kv head),
+ * ascending, each group padded with empty items (k0 = k1 = 0) to a multiple of 4: four consecutive
+ * items run as one workgroup, which merges their partials.  comb_off [comb_cap] receives the first
+ * item of (seq b, kv head g) at b * num_kv_heads + g and the item count at num_seqs * num_kv_heads.
+ * *n_items = 0 when the tables are not decode-shaped (a sequence with more than one query row, or
+ * more than 16 q heads per KV head).  Any output pointer may be NULL. */
 rk_status rk_seg_tables_decode_schedule(const rk_tables *tables, int32_t layer, int32_t *items, int64_t cap,
                                         int64_t *n_items, int32_t *comb_off, int64_t comb_cap);
 

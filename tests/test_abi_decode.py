@@ -129,24 +129,30 @@ def test_decode_items_cover_the_visible_keys_once(seed):
             if not n_new[b]:
                 assert len(mine) == 0
                 continue
+            # four items per workgroup, all of one (seq, kv head): empty items (0, 0) pad the last group
+            assert len(mine) % 4 == 0 and comb[b * Hkv + g] % 4 == 0
+            real = mine[mine[:, 3] > mine[:, 2]]
+            pad = mine[len(real):]
+            assert (pad[:, 2:] == 0).all() and len(pad) < 4, "padding only closes the group"
             vis = attention.visibility_mask(int(c["hc"][0, g]), np.array([L - 1]), L, c["S"], c["W"])[0]
             cover = np.zeros(L, np.int64)
-            for _, _, k0, k1 in mine.tolist():
+            for _, _, k0, k1 in real.tolist():
                 assert 0 <= k0 < k1 <= L
                 cover[k0:k1] += 1
             assert (cover == vis.astype(np.int64)).all(), "items must cover each visible key exactly once"
-            ks = mine[:, 2:].tolist()
+            ks = real[:, 2:].tolist()
             assert ks == sorted(ks)
-    # one key chunk, aiming the layer at 4096 items: a multiple of 32, at least 256; no item crosses
+    # one key chunk, aiming the layer at 8192 items: a multiple of 32, at least 128; no item crosses
     # a multiple of it
     keys = sum(int(attention.visibility_mask(int(c["hc"][0, g]), np.array([L - 1]), L, c["S"], c["W"]).sum())
                for b, L in enumerate(c["kv"]) if n_new[b] for g in range(Hkv))
     ranges = sum(len(_ranges(int(c["hc"][0, g]), L, c["S"], c["W"])) for b, L in enumerate(c["kv"]) if n_new[b]
                  for g in range(Hkv))
-    room = max(4096 // 4, 4096 - 2 * ranges)
-    chunk = max(256, -(-(-(-keys // room)) // 32) * 32)
-    assert len(items) <= 4096 or room == 4096 // 4
-    for _, _, k0, k1 in items.tolist():
+    room = max(8192 // 4, 8192 - 2 * ranges)
+    chunk = max(128, -(-(-(-keys // room)) // 32) * 32)
+    real = items[items[:, 3] > items[:, 2]]
+    assert len(real) <= 8192 or room == 8192 // 4
+    for _, _, k0, k1 in real.tolist():
         assert k0 // chunk == (k1 - 1) // chunk
     rk_seg.rk_seg_tables_destroy(t)
     rk_seg.rk_seg_pool_destroy(pool)
@@ -159,7 +165,7 @@ def test_prefill_shaped_tables_have_no_decode_items():
     assert len(items) == 0 and comb is None
     rk_seg.rk_seg_tables_advance(t, [1], device=False)
     items, comb = rk_seg.rk_seg_tables_decode_schedule(t, 0)
-    assert len(items) >= 2 and comb[-1] == len(items)
+    assert len(items) >= 4 and len(items) % 4 == 0 and comb[-1] == len(items)
     rk_seg.rk_seg_tables_destroy(t)
     rk_seg.rk_seg_pool_destroy(pool)
 
