@@ -74,6 +74,21 @@ def useful_flops(stats: dict, head_dim: int) -> float:
     return 4.0 * head_dim * stats["visible_pairs"]
 
 
+def hbm_rates(wl, stats: dict, ms: float) -> dict:
+    """HBM rates of one attention launch against the 8 TB/s peak.  Algorithmic bytes: q and o once, lse,
+    and every held K/V page once.  Tile bytes: the K/V tiles the item list stages (each item reads its
+    tiles; several items of one (seq, KV head) read the same tile, mostly from L2)."""
+    elem = 2 if wl.dtype == torch.bfloat16 else 4
+    D = wl.head_dim
+    algo = (2 * wl.total_q * wl.num_q_heads * D * elem + 4 * wl.num_q_heads * wl.total_q
+            + stats["pages_held"] * wl.page_size * D * elem * 2)
+    tile = stats["key_tiles"] * 2 * 64 * D * elem
+    t = ms * 1e-3
+    return {"algorithmic_bytes": algo, "tile_bytes": tile, "algorithmic_gbs": algo / t / 1e9,
+            "tile_gbs": tile / t / 1e9, "pct_hbm_peak_algorithmic": 100.0 * algo / t / 1e9 / PEAK_HBM_GBS,
+            "pct_hbm_peak_tile": 100.0 * tile / t / 1e9 / PEAK_HBM_GBS}
+
+
 class Bench:
     """Runs steps of one workload with inputs resident in HBM."""
 
@@ -234,6 +249,7 @@ def run_workload(wl, steps: int, warmup: int, with_dense: bool):
         "ms_per_step": ms_step,
         "ms_attention": float(np.mean(b.attn_ms)),
         "ms_attention_min": float(np.min(b.attn_ms)),
+        "ms_attention_median": float(np.median(b.attn_ms)),
         "ms_append": float(np.mean(b.append_ms)),
         "ms_import": float(np.mean(b.import_ms)),
         "useful_tflop": flops / 1e12,
@@ -245,6 +261,7 @@ def run_workload(wl, steps: int, warmup: int, with_dense: bool):
     res["tflops_step"] = flops / (ms_step * 1e-3) / 1e12
     res["tflops_attention"] = flops / (res["ms_attention"] * 1e-3) / 1e12
     res["pct_mfma_peak_attention"] = 100.0 * res["tflops_attention"] / PEAK_BF16_TFLOPS
+    res["hbm"] = hbm_rates(wl, b.stats, res["ms_attention"])
     log("  mixed: %.3f ms/step, attention %.3f ms, %.1f useful TFLOP/s (%.1f%% of bf16 peak)" % (
         ms_step, res["ms_attention"], res["tflops_attention"], res["pct_mfma_peak_attention"]))
     if wl.group <= 16 and wl.dtype == torch.bfloat16:
@@ -289,6 +306,51 @@ def run_workload(wl, steps: int, warmup: int, with_dense: bool):
     del inp, b, runner
     torch.cuda.empty_cache()
     return res
+
+
+def sweep(steps: int, warmup: int) -> dict:
+    """Does layer time track visible pairs (not H x L)?  At the 128K Qwen3-32B shape (one sequence,
+    64 q / 8 KV heads, page 64, sink 4), sweep the window over {1024, 2048, 4096, 8192} and the number of
+    GLOBAL KV heads over {0 (all LOCAL), 1, 2, 4, 8 (all GLOBAL)}, on the same q/k/v, and fit
+    t = a + b * pairs by least squares.  Each configuration: `warmup` untimed and `steps` timed calls,
+    median and minimum of the attention launch (HIP events on the kernel's stream)."""
+    base = workloads.qwen32b()
+    L = base.layer
+    wl_all = base.with_classes(np.ones_like(base.head_class))
+    pages = workloads.pool_pages_needed_hint(wl_all) + base.pool_slack
+    inp = workloads.make_inputs(base, device="cuda", num_pages=pages)
+    rows = []
+    for W in (1024, 2048, 4096, 8192):
+        for ng in (0, 1, 2, 4, 8):
+            hc = np.zeros_like(base.head_class)
+            hc[L, :ng] = 1
+            wl = dataclasses.replace(base.with_classes(hc, "%s W=%d global=%d" % (base.name, W, ng)), window=W)
+            r = PrefillRunner(wl, free_order=inp.free_order)
+            b = Bench(wl, dataclasses.replace(inp, wl=wl), r)
+            b.run(steps, warmup)
+            r.close()
+            ms = float(np.median(b.attn_ms))
+            fl = useful_flops(b.stats, wl.head_dim)
+            row = {"window": W, "global_kv_heads": ng, "visible_pairs": b.stats["visible_pairs"],
+                   "ms_attention_median": ms, "ms_attention_min": float(np.min(b.attn_ms)),
+                   "useful_tflops": fl / (ms * 1e-3) / 1e12, "pct_mfma_peak": 100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                   "hbm": hbm_rates(wl, b.stats, ms)}
+            rows.append(row)
+            log("  W=%5d global=%d: %.3f ms (min %.3f), %.3e pairs, %.1f TFLOP/s (%.1f%%), HBM %.0f GB/s "
+                "algorithmic, %.0f GB/s tile" % (W, ng, ms, row["ms_attention_min"], row["visible_pairs"],
+                                                 row["useful_tflops"], row["pct_mfma_peak"],
+                                                 row["hbm"]["algorithmic_gbs"], row["hbm"]["tile_gbs"]))
+            del b
+    del inp
+    torch.cuda.empty_cache()
+    x = np.array([r["visible_pairs"] for r in rows], np.float64)
+    y = np.array([r["ms_attention_median"] for r in rows], np.float64)
+    slope, icpt = np.polyfit(x, y, 1)
+    pred = icpt + slope * x
+    r2 = 1.0 - float(((y - pred) ** 2).sum()) / float(((y - y.mean()) ** 2).sum())
+    log("  fit: t = %.3f ms + %.4e ms/pair * pairs, R^2 = %.5f" % (icpt, slope, r2))
+    return {"workload": base.name + " (window and GLOBAL-head sweep)", "steps": steps, "warmup": warmup,
+            "rows": rows, "fit": {"intercept_ms": icpt, "ms_per_pair": slope, "r2": r2}}
 
 
 def cpu_baseline(wl, budget_s: float = 15.0):
@@ -388,6 +450,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the dense reference and the two 128K calls (Qwen3-32B-shaped, EXECUTE split)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line: the window x GLOBAL-head sweep at the 128K shape, "
+                         "with a fit of layer time against visible pairs (one JSON line)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size HBM reference for counters)")
     a = ap.parse_args()
@@ -406,6 +471,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if a.sweep:
+        print(json.dumps({"sweep": sweep(a.steps, a.warmup)}), flush=True)
+        return
     wl = workloads.CONFIGS[a.workload]()
     main_res = run_workload(wl, a.steps, a.warmup, with_dense=not a.no_extra)
     extra = {}
@@ -417,6 +485,10 @@ def main():
                                                              with_dense=True)
     cpu = None if a.no_cpu else cpu_baseline(wl, a.cpu_seconds)
     if cpu is not None:
+        # the whole layer at the sampled rate: extrapolated, not measured
+        cpu["extrapolated_layer_s"] = main_res["useful_tflop"] / cpu["value"]
+        log("  oracle on the host: %.4f TFLOP/s on %d threads; the whole layer would take %.0f s (extrapolated)" % (
+            cpu["value"], cpu["cores"], cpu["extrapolated_layer_s"]))
         main_res["cpu_oracle_beside"] = cpu_next_baselines(wl)
         log("  oracle on the host: decode %.2f GB/s, per-key mass %.4f TFLOP/s" % (
             main_res["cpu_oracle_beside"]["decode"]["value"], main_res["cpu_oracle_beside"]["key_mass"]["value"]))
