@@ -6,14 +6,15 @@
 // 长上下文大模型推理引擎" (shshi.cn), section RedKnot技术原理, 3).
 //
 // Design: key-stationary, so that every output is written once (a query-stationary pass would need
-// one global atomic per (head, key, query tile)).  A workgroup owns kMassKeys = 256 keys of one
-// (sequence, KV head); each of its eight waves holds the K fragments of 32 keys in registers.  It
-// steps over the call's query tokens in blocks of 256 rows (G heads x 256/G tokens, the rows of an
-// attention work item): the rows are staged in LDS by direct 16-byte global->LDS loads (double-
-// buffered, XOR-swizzled as in the attention kernel), with lse * log2(e) beside them.  S = Q K^T runs
-// on v_mfma_f32_32x32x16_bf16 with keys as the N dimension, so each lane owns one key and sums its
-// weights over the 16 query rows it holds; the two half-waves are combined with v_permlane32_swap
-// and per-head sums go to LDS accumulators (ds_add_f32 on distinct keys), written to HBM at the end.
+// one global atomic per (head, key, query tile)).  A workgroup owns 8 KPW keys of one (sequence, KV
+// head); each of its eight waves holds the K fragments of KPW keys in registers (KPW = 64 when G <= 8,
+// else 32).  It steps over the call's query tokens in steps of 256 rows (G heads x T tokens, T the
+// largest multiple of 16 with G T <= 256): the rows are staged in LDS by direct 16-byte global->LDS
+// loads (double-buffered, XOR-swizzled as in the attention kernel), with lse * log2(e) beside them.
+// S = Q K^T runs on v_mfma_f32_32x32x16_bf16 with keys as the N dimension, so each lane owns one key
+// and sums its weights over the 16 query rows it holds; the two half-waves are combined with
+// v_permlane32_swap and per-head sums go to LDS accumulators (ds_add_f32 on distinct keys), which the
+// workgroup adds to the zero-filled output at the end (one global atomic per (head, key, query chunk)).
 // Rows outside the call (past kv_len, or of a LOCAL head below its start) read a valid row and get
 // lse = +inf, so their weight is exactly 0; the visibility mask (causal, sink, window) comes from
 // indices, on edge blocks only.
