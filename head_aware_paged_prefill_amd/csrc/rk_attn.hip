@@ -54,7 +54,7 @@ constexpr float kRescaleSlack = 8.0f;  // log2 of the largest un-normalised weig
 #define RK_TILES_PER_STEP 2  // key tiles staged per LDS buffer and barrier step
 #endif
 
-// LDS image of one 64-key tile, filled by direct 16-byte loads into LDS (lane l of a load
+// LDS image of one 64-key tile, filled by direct global->LDS 16-byte loads (lane l of a load
 // writes bytes [16 l, 16 l + 16) of a 1 KB block, so every block is dense: rows cannot be padded
 // and bank conflicts are avoided by choosing, per lane, which 16-byte chunk of the row it fetches).
 //  K: 64 rows of D channels in MFMA row order (key index with bits 2 and 3 swapped); chunk c of
