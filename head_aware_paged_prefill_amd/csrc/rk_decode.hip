@@ -49,7 +49,8 @@ struct DecTile {
   u32x2 vb[D / 16];     // the same, keys kt + 16 + 4 (lane / 16) .. + 3
 };
 
-template <int D>
+// SMALLP: 8-key pages, where a 16-key half of a tile spans two pages (each lane picks its page)
+template <int D, bool SMALLP>
 __global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p) {
   constexpr int KS = D / 32;  // 32-channel steps of QK
   constexpr int DT = D / 16;  // 16-channel tiles of PV
@@ -69,11 +70,15 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p)
     const int pg = pt[min(key, L - 1) >> p.log2P];
     return key < L && pg >= 0 ? pg : pg0;
   };
-  // page ids of a tile's two 16-key halves, looked up two tiles before its loads are issued
+  // page ids of a tile's two 16-key halves (with 8-key pages: of its four 8-key quarters), looked up
+  // two tiles before its loads are issued
   struct Pages {
-    int a, b;
+    int a, b, a1, b1;
   };
-  auto pages_of = [&](int kt) { return Pages{page_of(kt), page_of(kt + 16)}; };
+  auto pages_of = [&](int kt) {
+    if constexpr (SMALLP) return Pages{page_of(kt), page_of(kt + 16), page_of(kt + 8), page_of(kt + 24)};
+    else return Pages{page_of(kt), page_of(kt + 16), 0, 0};
+  };
 
   // Q as the B operand of S^T: lane holds channels 32 ks + 8 q4 .. + 7 of row c16 (q head g G + c16)
   bf16x8 qf[KS];
@@ -92,6 +97,27 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p)
   const uint32_t k_lane = (uint32_t)((c16 * D + 8 * q4) * 2);  // bytes within a 16-key block of a K page
   const uint32_t v_lane = (uint32_t)((c16 * P + 4 * q4) * 2);  // bytes within a 16-channel block of a V page
   auto load = [&](int kt, Pages pg, DecTile<D> &T) {  // pg: uniform; a == b when P >= 32
+    if constexpr (SMALLP) {
+      // K row c16 of a half: key 16 h + c16, page a / a1 (b / b1) by c16 < 8; V run 4 q4 .. + 3: page
+      // by q4 < 2, slot (4 q4) % 8.  Per-lane 64-bit addresses.
+      const int64_t ra = c16 < 8 ? pg.a : pg.a1, rb = c16 < 8 ? pg.b : pg.b1;
+      const char *ka = kbytes + ((ra * 8 + (c16 & 7)) * D + 8 * q4) * 2;
+      const char *kb = kbytes + ((rb * 8 + (c16 & 7)) * D + 8 * q4) * 2;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        T.k[0][ks] = *reinterpret_cast<const bf16x8 *>(ka + 64 * ks);
+        T.k[1][ks] = *reinterpret_cast<const bf16x8 *>(kb + 64 * ks);
+      }
+      const int64_t qa = q4 < 2 ? pg.a : pg.a1, qb = q4 < 2 ? pg.b : pg.b1;
+      const char *va = vbytes + (qa * D * 8 + c16 * 8 + ((4 * q4) & 7)) * 2;
+      const char *vb = vbytes + (qb * D * 8 + c16 * 8 + ((4 * q4) & 7)) * 2;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        T.va[dt] = *reinterpret_cast<const u32x2 *>(va + dt * 16 * 8 * 2);
+        T.vb[dt] = *reinterpret_cast<const u32x2 *>(vb + dt * 16 * 8 * 2);
+      }
+      return;
+    }
     const int sa = kt & (P - 1), sb = (kt + 16) & (P - 1);
     const char *ka = kbytes + ((int64_t)pg.a * P + sa) * D * 2;
     const char *kb = kbytes + ((int64_t)pg.b * P + sb) * D * 2;
@@ -284,11 +310,14 @@ hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t stream
   if (p.n_items <= 0) return hipSuccess;
   if (p.n_items % kDecodeWaves) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p.n_items / kDecodeWaves)), comb((unsigned)(p.num_seqs * p.Hkv * p.G));
+  const dim3 block(64 * kDecodeWaves);
   if (head_dim == 128) {
-    hipLaunchKernelGGL(decode_bf16<128>, grid, dim3(64 * kDecodeWaves), 0, stream, p);
+    if (p.P < 16) hipLaunchKernelGGL((decode_bf16<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_bf16<128, false>), grid, block, 0, stream, p);
     hipLaunchKernelGGL(decode_combine<128>, comb, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(decode_bf16<64>, grid, dim3(64 * kDecodeWaves), 0, stream, p);
+    if (p.P < 16) hipLaunchKernelGGL((decode_bf16<64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_bf16<64, false>), grid, block, 0, stream, p);
     hipLaunchKernelGGL(decode_combine<64>, comb, dim3(256), 0, stream, p);
   }
   return hipGetLastError();

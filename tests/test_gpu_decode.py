@@ -122,7 +122,7 @@ def test_decode_long_context_splits_and_combines():
     decode_parity(wl, 4, wl.name)
 
 
-@pytest.mark.parametrize("G,D,P", [(16, 64, 16), (8, 64, 256), (2, 128, 128)])
+@pytest.mark.parametrize("G,D,P", [(16, 64, 16), (8, 64, 256), (2, 128, 128), (4, 64, 8), (16, 128, 8)])
 def test_decode_shapes(G, D, P):
     wl = workloads.random_small(4, torch.bfloat16)
     wl = dataclasses.replace(wl, num_q_heads=G * wl.num_kv_heads, head_dim=D, page_size=P,

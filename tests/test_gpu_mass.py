@@ -91,6 +91,14 @@ def test_mass_odd_and_large_groups(G):
     mass_parity(wl, wl.name)
 
 
+@pytest.mark.parametrize("P,D", [(8, 64), (8, 128), (256, 128)])
+def test_mass_page_sizes(P, D):
+    # 8-key pages (the smallest the pool takes) and 256-key pages: the kernel looks up each key's page
+    wl = workloads.random_small(4, torch.bfloat16)
+    wl = dataclasses.replace(wl, page_size=P, head_dim=D, name="mass P=%d D=%d" % (P, D))
+    mass_parity(wl, wl.name)
+
+
 @pytest.mark.parametrize("G", [8, 16])
 def test_mass_multi_chunk(G):
     # several key blocks and query chunks per head, so that the partial sums of many work units meet

@@ -290,7 +290,8 @@ def test_dsv4flash_layer_with_reuse_sampled():
 
 
 @pytest.mark.parametrize("seed,P,G,D", [(2, 8, 2, 64), (5, 128, 4, 128), (6, 256, 1, 128), (12, 16, 3, 64),
-                                        (13, 32, 16, 128), (14, 64, 5, 64), (15, 256, 8, 64)])
+                                        (13, 32, 16, 128), (14, 64, 5, 64), (15, 256, 8, 64), (3, 8, 8, 128),
+                                        (7, 8, 1, 128)])
 def test_edge_shapes(seed, P, G, D):
     wl = workloads.random_small(seed, torch.bfloat16)
     wl = dataclasses.replace(wl, page_size=P, num_q_heads=G * wl.num_kv_heads, head_dim=D,
