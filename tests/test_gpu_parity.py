@@ -299,6 +299,18 @@ def test_edge_shapes(seed, P, G, D):
     full_parity(wl, wl.name)
 
 
+@pytest.mark.parametrize("G,D,dtype", [(32, 128, torch.bfloat16), (64, 64, torch.bfloat16), (100, 128, torch.bfloat16),
+                                       (256, 64, torch.bfloat16), (48, 64, torch.float32)])
+def test_large_groups(G, D, dtype):
+    # up to 256 q heads per KV head (T = 256 / G tokens per work item, down to one); a GLOBAL and a LOCAL
+    # KV head, reused prefix on the second sequence
+    wl = workloads.Workload(name="G=%d D=%d %s" % (G, D, str(dtype).split(".")[-1]), config_id=430 + G, num_layers=1,
+                            layer=0, kv_lens=[300, 77], q_starts=[0, 40], num_q_heads=2 * G, num_kv_heads=2, head_dim=D,
+                            page_size=16, sink=4, window=100, dtype=dtype, head_class=np.array([[1, 0]], np.uint8),
+                            pool_slack=7, doc_len=50, rope_base=1.0e4)
+    full_parity(wl, wl.name)
+
+
 def test_empty_batch_and_zero_query_sequence():
     wl = workloads.random_small(4, torch.bfloat16, allow_reuse=False)
     # a sequence whose queries were all served earlier sits next to a normal one
