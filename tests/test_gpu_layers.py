@@ -1,0 +1,71 @@
+"""One tables object over several layers (rk_seg_build_tables over [layer_begin, layer_end)), each layer with
+its own head classes and its own q/k/v: the prefill call of every layer against the fp64 oracle, then trim,
+one token per sequence (rk_seg_tables_advance, all layers at once) and a decode step of every layer against the
+oracle's decode row.  A layer that reads another layer's pages or classes fails (page "小红书把 KV Cache 按
+「头」拆了…" (zhichai.net), section 事件内容: the cache is paged per (layer, head)).  Bars: the attention parity
+bars."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from head_aware_paged_prefill_amd.runner import PrefillRunner
+from oracle import decode, reference
+
+from test_gpu_parity import check, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NL = 3
+
+
+def _layer_inputs(base, pages):
+    # each layer its own draw (config id per layer) and its own row of the class map
+    return [workloads.make_inputs(dataclasses.replace(base, layer=l, config_id=base.config_id + l), num_pages=pages)
+            for l in range(NL)]
+
+
+def test_three_layers_one_tables_prefill_then_decode():
+    base = workloads.Workload(name="3 layers", config_id=450, num_layers=NL, layer=0, kv_lens=[420, 130],
+                              q_starts=[0, 60], num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16, sink=4,
+                              window=96, dtype=torch.bfloat16,
+                              head_class=np.array([[1, 0], [0, 0], [1, 1]], np.uint8), pool_slack=7, doc_len=50,
+                              rope_base=1.0e4)
+    B, H, Hkv, D = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_dim
+    pages = NL * (workloads.pool_pages_needed_hint(base) + 2 * B * Hkv) + base.pool_slack
+    inps = _layer_inputs(base, pages)
+    say("3 layers: kv_lens=%s q_starts=%s classes=%s" % (base.kv_lens, base.q_starts, base.head_class.tolist()))
+    r = PrefillRunner(base, free_order=inps[0].free_order, poison=True)
+    try:
+        r.build(0, NL)
+        outs = []
+        for l in range(NL):
+            d = to_dev(inps[l])
+            r.import_docs(d.docs, layer=l)
+            outs.append(r.attend(d.q, d.k_new, d.v_new, layer=l))
+        torch.cuda.synchronize()
+        for l in range(NL):
+            o_ref, lse_ref = reference.prefill(inps[l])
+            check(outs[l][0], outs[l][1], o_ref, lse_ref, base.dtype, "layer %d prefill" % l)
+        r.trim()
+        r.advance([1] * B)
+        for l in range(NL):
+            wl_l = inps[l].wl
+            q, k, v = workloads.decode_inputs(wl_l, l, B)
+            o, lse = r.decode(q.cuda(), k.cuda(), v.cuda(), layer=l)
+            torch.cuda.synchronize()
+            o_ref = np.zeros((B, H, D))
+            lse_ref = np.zeros((H, B))
+            for b in range(B):
+                ks, vs = [], []
+                for g in range(Hkv):
+                    kh, vh = reference.head_kv(inps[l], b, g)
+                    ks.append(np.vstack([kh, k[b, g].double().numpy()[None]]))
+                    vs.append(np.vstack([vh, v[b, g].double().numpy()[None]]))
+                o_ref[b], lse_ref[:, b] = decode.decode_step(q[b].double().numpy(), ks, vs, base.head_class[l],
+                                                             base.sink, base.window)
+            check(o, lse, o_ref, lse_ref, base.dtype, "layer %d decode" % l)
+    finally:
+        r.close()
