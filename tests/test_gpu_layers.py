@@ -1,9 +1,9 @@
 """One tables object over several layers (rk_seg_build_tables over [layer_begin, layer_end)), each layer with
-its own head classes and its own q/k/v: the prefill call of every layer against the fp64 oracle, then trim,
-one token per sequence (rk_seg_tables_advance, all layers at once) and a decode step of every layer against the
-oracle's decode row.  A layer that reads another layer's pages or classes fails (page "小红书把 KV Cache 按
-「头」拆了…" (zhichai.net), section 事件内容: the cache is paged per (layer, head)).  Bars: the attention parity
-bars."""
+its own head classes and its own q/k/v: the prefill call and the per-key mass of every layer against the fp64
+oracle, then trim, one token per sequence (rk_seg_tables_advance, all layers at once) and a decode step of every
+layer against the oracle's decode row.  A layer that reads another layer's pages or classes fails (page "小红书
+把 KV Cache 按「头」拆了…" (zhichai.net), section 事件内容: the cache is paged per (layer, head)).  Bars: the
+attention parity bars; the mass within 2e-3 * max(1, mass) (the GPU's own lse)."""
 import dataclasses
 
 import numpy as np
@@ -45,10 +45,16 @@ def test_three_layers_one_tables_prefill_then_decode():
             d = to_dev(inps[l])
             r.import_docs(d.docs, layer=l)
             outs.append(r.attend(d.q, d.k_new, d.v_new, layer=l))
+        # the per-key mass of every layer, over that layer's call (its q and the GPU's lse)
+        masses = [r.key_mass(to_dev(inps[l]).q, outs[l][1], layer=l) for l in range(NL)]
         torch.cuda.synchronize()
         for l in range(NL):
             o_ref, lse_ref = reference.prefill(inps[l])
             check(outs[l][0], outs[l][1], o_ref, lse_ref, base.dtype, "layer %d prefill" % l)
+            want = reference.key_mass(inps[l])
+            got = masses[l].double().cpu().numpy()
+            err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+            assert err.max() <= 2e-3, "layer %d mass: rel err %.3g" % (l, err.max())
         r.trim()
         r.advance([1] * B)
         for l in range(NL):
@@ -69,3 +75,32 @@ def test_three_layers_one_tables_prefill_then_decode():
             check(o, lse, o_ref, lse_ref, base.dtype, "layer %d decode" % l)
     finally:
         r.close()
+
+
+def test_the_call_on_a_side_stream():
+    # every step of the call enqueued on a non-default stream (torch's current stream inside the block):
+    # the tables upload, the reuse import, the append and attention, the mass pass; only that stream is
+    # synchronised before the outputs are read
+    wl = workloads.random_small(3, torch.bfloat16)
+    inp = workloads.make_inputs(wl)
+    say("side stream: kv_lens=%s q_starts=%s" % (wl.kv_lens, wl.q_starts))
+    o_ref, lse_ref = reference.prefill(inp)
+    want = reference.key_mass(inp)
+    dinp = to_dev(inp)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        r = PrefillRunner(wl, free_order=inp.free_order, poison=True)
+        try:
+            r.build()
+            r.import_docs(dinp.docs)
+            o, lse = r.attend(dinp.q, dinp.k_new, dinp.v_new)
+            mass = r.key_mass(dinp.q, lse)
+            s.synchronize()
+            check(o, lse, o_ref, lse_ref, wl.dtype, "side stream")
+            got = mass.double().cpu().numpy()
+            err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+            assert err.max() <= 2e-3, "side stream mass: rel err %.3g" % err.max()
+        finally:
+            s.synchronize()
+            r.close()
