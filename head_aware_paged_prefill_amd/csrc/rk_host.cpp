@@ -1002,6 +1002,10 @@ rk_status rk_seg_reuse_rerotate(rk_pool *pool, const rk_tables *t, int32_t layer
     return fail(RK_ERR_INVALID_ARG, "src_k / src_v null or not 16-byte aligned");
   const int32_t D = pool->desc.head_dim;
   if (src_head_stride < (int64_t)n_tok * D) return fail(RK_ERR_INVALID_ARG, "src_head_stride < n_tok * head_dim");
+  const int64_t elem = pool->desc.dtype == RK_F32 ? 4 : 2;
+  if ((src_head_stride * elem) % 16)
+    return fail(RK_ERR_INVALID_ARG, "src_head_stride %lld elements is not a multiple of 16 bytes",
+                (long long)src_head_stride);
   if (!(rope_base > 1.0) || !std::isfinite(rope_base)) return fail(RK_ERR_INVALID_ARG, "rope_base must be > 1");
   if (rope_style != RK_ROPE_ROTATE_HALF && rope_style != RK_ROPE_INTERLEAVED)
     return fail(RK_ERR_INVALID_ARG, "rope_style %d", rope_style);
@@ -1016,6 +1020,11 @@ rk_status rk_seg_reuse_rerotate(rk_pool *pool, const rk_tables *t, int32_t layer
   p.delta = delta;
   p.rope_base = rope_base;
   p.rope_style = rope_style;
+  for (int m = 0; m < D / 2; ++m) {  // the angle, its cos and sin in fp64, rounded to fp32
+    const double a = (double)delta * std::pow(rope_base, -2.0 * (double)m / (double)D);
+    p.rope_cos[m] = (float)std::cos(a);
+    p.rope_sin[m] = (float)std::sin(a);
+  }
   int n_pages = (tok_begin + n_tok - 1) / t->P - p.page0 + 1;
   hipError_t e = rk::launch_import(p, n_pages, pool->desc.dtype, D, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "re-rotate kernel launch");

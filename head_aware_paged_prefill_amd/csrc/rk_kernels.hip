@@ -48,7 +48,6 @@ __global__ void __launch_bounds__(256) kv_write(KvWriteParams p) {
   constexpr int VEC = Vec16<T>::N;
   constexpr int VPITCH = D + 1;
   __shared__ T sv[kTokBlock * VPITCH];
-  __shared__ float cs[D / 2], sn[D / 2];
 
   const int tid = threadIdx.x;
   const int g = blockIdx.y;
@@ -58,8 +57,11 @@ __global__ void __launch_bounds__(256) kv_write(KvWriteParams p) {
   if (IMPORT) {
     seq = p.seq;
     lp = p.page0 + blockIdx.x;
+    si = p.seqs[seq];
+    // tokens from the head's class start on are the call's own (its append writes them): not imported
+    const int start = p.head_class[g] == RK_GLOBAL ? si.q_start : si.q_start_local;
     t_lo = max(lp * P, p.tok_begin);
-    t_hi = min(lp * P + P, p.tok_begin + p.n_tok);
+    t_hi = min(min(lp * P + P, p.tok_begin + p.n_tok), start);
   } else {
     seq = p.app_items[2 * blockIdx.x];
     lp = p.app_items[2 * blockIdx.x + 1];
@@ -82,16 +84,6 @@ __global__ void __launch_bounds__(256) kv_write(KvWriteParams p) {
   T *kdst = static_cast<T *>(p.k_pages) + ((int64_t)pg * P + s0) * D;
   T *vdst = static_cast<T *>(p.v_pages) + (int64_t)pg * D * P;
 
-  if (IMPORT) {
-    for (int mm = tid; mm < D / 2; mm += blockDim.x) {
-      const double th = pow(p.rope_base, -2.0 * (double)mm / (double)D);
-      const double a = (double)p.delta * th;
-      cs[mm] = (float)cos(a);
-      sn[mm] = (float)sin(a);
-    }
-    __syncthreads();
-  }
-
   // K
   if (!IMPORT) {
     for (int c = tid; c < n * (D / VEC); c += blockDim.x) {
@@ -100,16 +92,36 @@ __global__ void __launch_bounds__(256) kv_write(KvWriteParams p) {
           *reinterpret_cast<const u32x4 *>(src_row(ksrc, t_lo + tk) + ch * VEC);
     }
   } else {
-    for (int c = tid; c < n * (D / 2); c += blockDim.x) {
-      const int tk = c / (D / 2), mm = c - tk * (D / 2);
-      const int ia = p.rope_style == RK_ROPE_ROTATE_HALF ? mm : 2 * mm;
-      const int ib = p.rope_style == RK_ROPE_ROTATE_HALF ? mm + D / 2 : 2 * mm + 1;
+    // VEC consecutive pairs per thread: rotate-half pairs (m, m + D/2) are two 16-byte runs of the
+    // row; interleaved pairs (2m, 2m + 1) are two consecutive 16-byte runs
+    constexpr int NJ = D / 2 / VEC;  // pair groups per row
+    typedef T TV __attribute__((ext_vector_type(VEC)));
+    for (int c = tid; c < n * NJ; c += blockDim.x) {
+      const int tk = c / NJ, j = c - tk * NJ, m0 = VEC * j;
       const T *s = src_row(ksrc, t_lo + tk);
-      const float xa = to_f(s[ia]), xb = to_f(s[ib]);
-      const float ya = xa * cs[mm] - xb * sn[mm];
-      const float yb = xb * cs[mm] + xa * sn[mm];
-      kdst[(int64_t)tk * D + ia] = from_f<T>(ya);
-      kdst[(int64_t)tk * D + ib] = from_f<T>(yb);
+      T *d = kdst + (int64_t)tk * D;
+      const bool half = p.rope_style == RK_ROPE_ROTATE_HALF;
+      const int oa = half ? m0 : 2 * m0, ob = half ? m0 + D / 2 : 2 * m0 + VEC;
+      const TV ra = *reinterpret_cast<const TV *>(s + oa), rb = *reinterpret_cast<const TV *>(s + ob);
+      TV wa, wb;
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        // pair k of the group: rotate-half (ra[k], rb[k]); interleaved (r[2k], r[2k + 1]) over ra | rb
+        const int m = m0 + k;
+        const float xa = to_f(half ? ra[k] : (2 * k < VEC ? ra[2 * k] : rb[2 * k - VEC]));
+        const float xb = to_f(half ? rb[k] : (2 * k + 1 < VEC ? ra[2 * k + 1] : rb[2 * k + 1 - VEC]));
+        const float ya = xa * p.rope_cos[m] - xb * p.rope_sin[m];
+        const float yb = xb * p.rope_cos[m] + xa * p.rope_sin[m];
+        if (half) {
+          wa[k] = from_f<T>(ya);
+          wb[k] = from_f<T>(yb);
+        } else {
+          if (2 * k < VEC) wa[2 * k] = from_f<T>(ya); else wb[2 * k - VEC] = from_f<T>(ya);
+          if (2 * k + 1 < VEC) wa[2 * k + 1] = from_f<T>(yb); else wb[2 * k + 1 - VEC] = from_f<T>(yb);
+        }
+      }
+      *reinterpret_cast<TV *>(d + oa) = wa;
+      *reinterpret_cast<TV *>(d + ob) = wb;
     }
   }
 
@@ -139,19 +151,37 @@ __global__ void __launch_bounds__(256) kv_write(KvWriteParams p) {
     }
   }
 
-  // V: transpose [tokens][D] -> page [D][P] through LDS, kTokBlock tokens at a time
+  // V: transpose [tokens][D] -> page [D][P] through LDS, kTokBlock tokens at a time.  Rows are read
+  // 16 bytes per thread; each channel row of the page is written in 16-byte groups of VEC slots where
+  // a group lies wholly inside the block's slots, element by element at the block's ragged ends.
+  typedef T TV __attribute__((ext_vector_type(VEC)));
   for (int tb = 0; tb < n; tb += kTokBlock) {
     const int nb = min(kTokBlock, n - tb);
     __syncthreads();
-    for (int c = tid; c < nb * D; c += blockDim.x) {
-      const int tk = c / D, d = c - tk * D;
-      sv[tk * VPITCH + d] = src_row(vsrc, t_lo + tb + tk)[d];
+    for (int c = tid; c < nb * (D / VEC); c += blockDim.x) {
+      const int tk = c / (D / VEC), ch = c - tk * (D / VEC);
+      const TV v = *reinterpret_cast<const TV *>(src_row(vsrc, t_lo + tb + tk) + ch * VEC);
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) sv[tk * VPITCH + ch * VEC + k] = v[k];
     }
     __syncthreads();
-    const int sa = s0 + tb;  // first slot of this block
-    for (int c = tid; c < nb * D; c += blockDim.x) {
-      const int d = c / nb, tk = c - d * nb;
-      vdst[(int64_t)d * P + sa + tk] = sv[tk * VPITCH + d];
+    const int sa = s0 + tb, se = sa + nb;      // slots [sa, se) of this block
+    const int g0 = (sa + VEC - 1) / VEC, g1 = se / VEC;  // whole VEC-slot groups inside
+    const int ng = max(0, g1 - g0);
+    for (int c = tid; c < ng * D; c += blockDim.x) {
+      const int d = c / ng, gi = g0 + (c - d * ng);
+      TV w;
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) w[k] = sv[(gi * VEC + k - sa) * VPITCH + d];
+      *reinterpret_cast<TV *>(vdst + (int64_t)d * P + gi * VEC) = w;
+    }
+    // ragged ends: slots [sa, g0 VEC) and [max(g1 VEC, sa), se) that no whole group covers
+    const int h0 = min(se, g0 * VEC), t0 = max(sa, max(g1, g0) * VEC);
+    const int nh = h0 - sa, nt = max(0, se - t0);  // no tail when the block lies inside one group
+    for (int c = tid; c < (nh + nt) * D; c += blockDim.x) {
+      const int d = c / (nh + nt), i = c - d * (nh + nt);
+      const int sl = i < nh ? sa + i : t0 + (i - nh);
+      vdst[(int64_t)d * P + sl] = sv[(sl - sa) * VPITCH + d];
     }
   }
 }

@@ -36,6 +36,10 @@ struct KvWriteParams {
   int64_t delta;
   double rope_base;
   int32_t rope_style;
+  // import: cos and sin of delta * base^(-2m/D) for pair m < D/2 (computed in fp64 on the host,
+  // rounded to fp32)
+  float rope_cos[64];
+  float rope_sin[64];
 };
 
 // Per-key attention mass of one layer's call (bf16 pools, G <= 16).  A workgroup of 8 waves owns

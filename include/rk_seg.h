@@ -271,8 +271,10 @@ rk_status rk_seg_tables_destroy(rk_pool *pool, rk_tables *tables);
  * into the held pages of every KV head of `layer`, rotating each key by delta = actual - offline
  * position: pair m turns by delta * base^(-2m/D) (angle, cos and sin in fp64, rotation in fp32, one
  * round-to-nearest-even store).  V is copied unchanged.  Tokens a head does not hold are skipped.
+ * Tokens at or after a head's class start (q_start_global for GLOBAL heads, q_start for LOCAL heads)
+ * are the call's own and are skipped too: the append inside rk_seg_attn_prefill writes them.
  * src_k, src_v: device [num_kv_heads][n_tok][head_dim] with head stride src_head_stride elements
- * (>= n_tok*head_dim); read only.  Requires tok_begin + n_tok <= kv_len[seq].
+ * (>= n_tok*head_dim, a multiple of 16 bytes); read only.  Requires tok_begin + n_tok <= kv_len[seq].
  * Errors: RK_ERR_INVALID_ARG, RK_ERR_STATE (host-only or trimmed tables), RK_ERR_HIP. */
 rk_status rk_seg_reuse_rerotate(rk_pool *pool, const rk_tables *tables, int32_t layer, int32_t seq,
                                 int32_t tok_begin, int32_t n_tok, const void *src_k, const void *src_v,

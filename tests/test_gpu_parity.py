@@ -44,14 +44,14 @@ def cleared_below_window(t, cls, start, kv_len, sink, window, page_size):
     return (t >= max(p0, sink)) & (t < min(start, start - window + 1))
 
 
-def run_call(inp, free_order=None, fill=float("nan")):
+def run_call(inp, free_order=None, fill=float("nan"), rope_style=rk_seg.RK_ROPE_ROTATE_HALF):
     wl = inp.wl
     fo = inp.free_order if free_order is None else free_order
     r = PrefillRunner(wl, free_order=fo, poison=False)
     r.k_pages.fill_(fill)
     r.v_pages.fill_(fill)
     r.build()
-    r.import_docs(inp.docs)
+    r.import_docs(inp.docs, rope_style=rope_style)
     o, lse = r.attend(inp.q, inp.k_new, inp.v_new)
     torch.cuda.synchronize()
     return r, o, lse
@@ -167,24 +167,30 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
-@pytest.mark.parametrize("seed", [1, 2, 4, 9, 11])
-def test_pages_hold_rerotated_prefix_and_appended_tokens(seed):
+@pytest.mark.parametrize("seed,style", [(1, rope.ROTATE_HALF), (2, rope.ROTATE_HALF), (4, rope.ROTATE_HALF),
+                                        (9, rope.ROTATE_HALF), (11, rope.ROTATE_HALF), (1, rope.INTERLEAVED),
+                                        (9, rope.INTERLEAVED)])
+def test_pages_hold_rerotated_prefix_and_appended_tokens(seed, style):
     wl = None
     s = seed
     while wl is None or all(q == 0 for q in wl.q_starts):  # need a reused prefix
         wl = workloads.random_small(s, torch.bfloat16)
         s += 100
     inp = workloads.make_inputs(wl)
-    say("page contents %s" % wl.name)
-    r, o, lse = run_call(to_dev(inp))
+    say("page contents %s style %d" % (wl.name, style))
+    kstyle = rk_seg.RK_ROPE_ROTATE_HALF if style == rope.ROTATE_HALF else rk_seg.RK_ROPE_INTERLEAVED
+    r, o, lse = run_call(to_dev(inp), rope_style=kstyle)
+    # the call's attention over the pages, against the oracle with the same pairing
+    o_ref, lse_ref = reference.prefill(inp, rope_style=style)
+    check(o, lse, o_ref, lse_ref, wl.dtype, "page contents %s style %d" % (wl.name, style))
     held = set()
     for b in range(wl.num_seqs):
-        k_ref, v_ref = reference.sequence_kv(inp, b)
+        k_ref, v_ref = reference.sequence_kv(inp, b, style)
         # exact rotation, not rounded: the kernel rounds once
         for d in inp.docs:
             if d.seq == b:
                 k_ref[:, d.tok_begin:d.tok_begin + d.n_tok] = rope.rotate(reference.to64(d.k_off), d.delta,
-                                                                           wl.rope_base)
+                                                                           wl.rope_base, style)
         for g in range(wl.num_kv_heads):
             kg, vg, toks = r.page_contents(0, g, b)
             _, ids = rk_seg.rk_seg_tables_export(r.tables, 0, g, b)

@@ -156,3 +156,58 @@ def test_dsv4flash_split_sampled():
         n += len(rows)
     assert n > 0
     r.close()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_import_stops_at_each_heads_class_start(seed):
+    # the reuse import alone (no append): below a head's class start its held slots hold the re-rotated
+    # document keys (within a bf16 ulp of the exact rotation) and the document values; from the class
+    # start on (a GLOBAL head's recomputed prefix) nothing is written -- the slots keep their poison
+    wl = workloads.random_split(seed, torch.bfloat16)
+    inp = workloads.make_inputs(wl)
+    dinp = to_dev(inp)
+    say("import stops at the class start: %s q_starts=%s qg=%s classes=%s" % (
+        wl.name, wl.q_starts, wl.q_starts_global, wl.head_class.tolist()))
+    r = PrefillRunner(wl, free_order=inp.free_order, poison=True)
+    try:
+        r.build()
+        r.import_docs(dinp.docs)
+        torch.cuda.synchronize()
+        for b in range(wl.num_seqs):
+            ref_k = np.full((wl.num_kv_heads, wl.kv_lens[b], wl.head_dim), np.nan)
+            ref_v = np.full_like(ref_k, np.nan)
+            for d in inp.docs:
+                if d.seq == b:
+                    ref_k[:, d.tok_begin:d.tok_begin + d.n_tok] = rope.rotate(reference.to64(d.k_off), d.delta,
+                                                                               wl.rope_base)
+                    ref_v[:, d.tok_begin:d.tok_begin + d.n_tok] = reference.to64(d.v_off)
+            for g in range(wl.num_kv_heads):
+                cls = int(wl.head_class[wl.layer, g])
+                start = wl.q_start_of(b, cls)
+                kg, vg, toks = r.page_contents(wl.layer, g, b)
+                t = np.array(toks)
+                kg, vg = kg.double().numpy(), vg.double().numpy()
+                doc = np.zeros(len(t), bool)
+                for d in inp.docs:
+                    if d.seq == b:
+                        doc |= (t >= d.tok_begin) & (t < d.tok_begin + d.n_tok)
+                below = doc & (t < start)
+                above = doc & (t >= start)
+                assert np.isnan(kg[above]).all() and np.isnan(vg[above]).all(), \
+                    "seq %d head %d: the import wrote tokens from the class start %d on" % (b, g, start)
+                kr, vr = ref_k[g, t[below]], ref_v[g, t[below]]
+                assert (np.abs(kg[below] - kr) <= bf16_ulp(kr)).all(), "re-rotated keys off by more than a bf16 ulp"
+                assert np.array_equal(vg[below], vr)
+        # the source head stride must keep 16-byte rows: a stride 3 elements past n_tok * D is rejected on
+        # the host, before any device access
+        d = dinp.docs[0]
+        Hkv, D = wl.num_kv_heads, wl.head_dim
+        if Hkv > 1:
+            st = d.n_tok * D + 3
+            buf = torch.zeros((Hkv * st,), dtype=wl.dtype, device="cuda")
+            odd = torch.as_strided(buf, (Hkv, d.n_tok, D), (st, D, 1))
+            with pytest.raises(rk_seg.RkError) as ei:
+                rk_seg.rk_seg_reuse_rerotate(r.tables, wl.layer, d.seq, d.tok_begin, odd, odd, d.delta, wl.rope_base)
+            assert ei.value.status == rk_seg.RK_ERR_INVALID_ARG
+    finally:
+        r.close()
