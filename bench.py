@@ -468,7 +468,7 @@ def cpu_next_baselines(wl, budget_s: float = 4.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama70b", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu", action="store_true")
