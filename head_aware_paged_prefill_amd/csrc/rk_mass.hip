@@ -13,8 +13,12 @@
 // loads (double-buffered, XOR-swizzled as in the attention kernel), with lse * log2(e) beside them.
 // S = Q K^T runs on v_mfma_f32_32x32x16_bf16 with keys as the N dimension, so each lane owns one key
 // and sums its weights over the 16 query rows it holds; the two half-waves are combined with
-// v_permlane32_swap and per-head sums go to LDS accumulators (ds_add_f32 on distinct keys), which the
-// workgroup adds to the zero-filled output at the end (one global atomic per (head, key, query chunk)).
+// v_permlane32_swap.  Each lane keeps one running total per (32-row block, key set) in registers over
+// all steps (a block's rows belong to the same head on every step), so the step loop does no LDS
+// writes besides the staged rows: an LDS add there would wait for the next step's direct loads, as
+// the compiler cannot tell their LDS area apart.  At the end the totals go to per-(head, key) LDS sums
+// (ds_add_f32), which the workgroup adds to the zero-filled output (one global atomic per (head, key,
+// query chunk)).
 // Rows outside the call (past kv_len, or of a LOCAL head below its start) read a valid row and get
 // lse = +inf, so their weight is exactly 0; the visibility mask (causal, sink, window) comes from
 // indices, on edge blocks only.
@@ -152,6 +156,12 @@ __global__ void __launch_bounds__(512, 1) key_mass_bf16(MassParams p) {
   auto head_of = [&](int k) { return (int)__builtin_popcount(hstart & ((2u << k) - 1u)) - 1; };
 
   const float c2 = p.scale_log2;
+  // per-lane totals of each (MFMA block, key set) over all steps: added to the LDS sums once, at the end
+  float accr[NRB][NS];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int st = 0; st < NS; ++st) accr[rb][st] = 0.f;
   // Weights of MFMA block (rb, key set st), summed per head: register i holds row rb 32 + 8 (i / 4)
   // + 4 hl + i % 4 of this lane's key, i < 8 in half 2 rb, i >= 8 in half 2 rb + 1.  Lane m gets
   // the first half's total over both lane halves, lane m + 32 the second's; both add to LDS.
@@ -184,8 +194,7 @@ __global__ void __launch_bounds__(512, 1) key_mass_bf16(MassParams p) {
     }
     // after the swap, r[0] + r[1] is lo of both lane halves on lanes < 32, hi of both on the rest
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
-    const float tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    atomicAdd(&sm.acc[(hl ? h1 : h0) * KEYS + KPW * wave + 32 * st + m], tot);
+    accr[rb][st] += __uint_as_float(r[0]) + __uint_as_float(r[1]);
   };
 
   // Two key sets per wave, every pair of the step visible (the common case: a wave's 64 keys straddle
@@ -218,9 +227,8 @@ __global__ void __launch_bounds__(512, 1) key_mass_bf16(MassParams p) {
       }
     };
     auto finish = [&](int rb, int st) {
-      const int h0 = head_of(2 * rb), h1 = head_of(2 * rb + 1);
       const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
-      atomicAdd(&sm.acc[(hl ? h1 : h0) * KEYS + KPW * wave + 32 * st + m], __uint_as_float(r[0]) + __uint_as_float(r[1]));
+      accr[rb][st] += __uint_as_float(r[0]) + __uint_as_float(r[1]);
       lo = hi = 0.f;
     };
 #pragma unroll
@@ -318,6 +326,14 @@ __global__ void __launch_bounds__(512, 1) key_mass_bf16(MassParams p) {
     if (more) lse_store(buf ^ 1);
     __syncthreads();
   }
+  // the lane totals into the per-(head, key) sums
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int h = hl ? head_of(2 * rb + 1) : head_of(2 * rb);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) atomicAdd(&sm.acc[h * KEYS + KPW * wave + 32 * st + m], accr[rb][st]);
+  }
+  __syncthreads();
   // partial sums of this query chunk: added to the zero-filled output
   for (int i = tid; i < G * KEYS; i += 512) {
     const int h = i / KEYS, kk = i - h * KEYS;
