@@ -333,6 +333,29 @@ def gemm_peak(n: int = 8192, reps: int = 20) -> dict:
             "tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12}
 
 
+def copy_peak(mib: int = 1024, reps: int = 10) -> dict:
+    """A measured HBM ceiling for copy-shaped kernels beside the 8 TB/s spec: a contiguous device-to-device copy
+    of `mib` MiB (torch's copy_), timed with HIP events, best of `reps`; bytes read plus bytes written."""
+    n = mib << 20
+    src = torch.empty((n,), dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    ms = float(np.min(ts))
+    return {"kind": "device-to-device copy of %d MiB via torch copy_, best of %d (read + write bytes)" % (mib, reps),
+            "ms": ms, "gbs": 2.0 * n / (ms * 1e-3) / 1e9}
+
+
 def sweep(steps: int, warmup: int) -> dict:
     """Does layer time track visible pairs (not H x L)?  At the 128K Qwen3-32B shape (one sequence,
     64 q / 8 KV heads, page 64, sink 4), sweep the window over {1024, 2048, 4096, 8192} and the number of
@@ -524,6 +547,13 @@ def main():
     main_res["measured_mfma_ceiling"] = gp
     log("  measured MFMA ceiling: %s: %.0f TFLOP/s (%.1f%% of spec); attention reaches %.1f%% of it" % (
         gp["kind"], gp["tflops"], 100.0 * gp["tflops"] / PEAK_BF16_TFLOPS, 100.0 * gp["attention_frac_of_it"]))
+    cp = copy_peak()
+    if "handoff" in main_res:
+        cp["handoff_frac_of_it"] = main_res["handoff"]["gbs"] / cp["gbs"]
+    main_res["measured_copy_ceiling"] = cp
+    log("  measured copy ceiling: %s: %.0f GB/s (%.1f%% of spec)%s" % (
+        cp["kind"], cp["gbs"], 100.0 * cp["gbs"] / PEAK_HBM_GBS,
+        "; the page hand-off reaches %.1f%% of it" % (100.0 * cp["handoff_frac_of_it"]) if "handoff" in main_res else ""))
     line = {
         "metric": METRIC,
         "value": round(main_res["tflops_step"], 3),
