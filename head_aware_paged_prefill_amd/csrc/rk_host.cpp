@@ -1025,7 +1025,25 @@ rk_status rk_seg_reuse_rerotate(rk_pool *pool, const rk_tables *t, int32_t layer
     p.rope_cos[m] = (float)std::cos(a);
     p.rope_sin[m] = (float)std::sin(a);
   }
-  int n_pages = (tok_begin + n_tok - 1) / t->P - p.page0 + 1;
+  // Launch over the logical pages some head imports: pages it holds in [tok_begin, its class start) of the
+  // document's range (a reused document below every LOCAL window and above the sink imports nothing, and
+  // under the split a GLOBAL head imports nothing).
+  int32_t lo = INT32_MAX, hi = -1;
+  for (int32_t g = 0; g < t->Hkv; ++g) {
+    const bool global = t->head_class[(size_t)layer * t->Hkv + g] == RK_GLOBAL;
+    const int32_t end = std::min(tok_begin + n_tok, global ? t->q_begin[seq] : t->q_start[seq]);
+    if (end <= tok_begin) continue;
+    const int64_t k = t->key(layer, g, seq);
+    const auto h0 = t->held_logical.begin() + t->held_off[k], h1 = t->held_logical.begin() + t->held_off[k + 1];
+    const auto first = std::lower_bound(h0, h1, tok_begin / t->P);
+    const auto last = std::upper_bound(first, h1, (end - 1) / t->P);
+    if (first == last) continue;
+    lo = std::min(lo, *first);
+    hi = std::max(hi, *(last - 1));
+  }
+  if (hi < 0) return RK_OK;
+  p.page0 = lo;
+  const int n_pages = hi - lo + 1;
   hipError_t e = rk::launch_import(p, n_pages, pool->desc.dtype, D, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "re-rotate kernel launch");
   return RK_OK;
