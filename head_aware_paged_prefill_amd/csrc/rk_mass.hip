@@ -274,11 +274,12 @@ __global__ void __launch_bounds__(512, 1) key_mass_bf16(MassParams p) {
     const int tmax = min(ts + T - 1, t_last);
     // per key set: some pair of the step visible / every pair visible
     bool any = false;
-    bool full[NS];
+    bool vis[NS], full[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const int kmin = kw + 32 * st, kmax = kmin + 31;
-      any = any || (kmin <= tmax && (global || kmin < SK || kmax > ts - W));
+      vis[st] = kmin <= tmax && (global || kmin < SK || kmax > ts - W);
+      any = any || vis[st];
       full[st] = kmax <= ts && (global || kmax < SK || kmin > tmax - W);
     }
     if (!any) return;  // no row of the step sees a key of this wave
@@ -288,6 +289,33 @@ __global__ void __launch_bounds__(512, 1) key_mass_bf16(MassParams p) {
     }
     const bf16_t *Qb = sm.q[buf];
     const float *l2 = sm.lse2[buf];
+    // one key set with no visible pair in the step (on the causal diagonal or the window edge): only
+    // the other set's products and weights
+    auto one_set = [&](auto stc) __attribute__((always_inline)) {
+      constexpr int st = decltype(stc)::value;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        bf16x8 a[NC];
+        const int qr = rb * 32 + m;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) a[c] = *reinterpret_cast<const bf16x8 *>(Qb + qr * D + (((2 * c + hl) ^ kswz<D>(qr)) << 3));
+        f32x16 sacc = {};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], kf[st][c], sacc, 0, 0, 0);
+        f32x4 lv[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) lv[q4] = *reinterpret_cast<const f32x4 *>(l2 + rb * 32 + 8 * q4 + 4 * hl);
+        reduce(rb, st, sacc, lv, full[st], ts);
+      }
+    };
+    if (NS == 2 && !vis[NS - 1]) {
+      one_set(IntC<0>{});
+      return;
+    }
+    if (NS == 2 && !vis[0]) {
+      one_set(IntC<NS - 1>{});
+      return;
+    }
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       bf16x8 a[NC];
