@@ -35,15 +35,35 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
+# largest finite bfloat16: (2 - 2^-7) * 2^127
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 values rounded once to bfloat16 (8 significant bits, the exponent range of fp32), to
+    nearest with ties to even, returned as fp64.  Written from the format's definition: the value is
+    scaled so that its bf16 quantum becomes 1, rounded half-to-even by np.rint, and scaled back (both
+    scalings are exact powers of two).  Below 2^-126 the quantum stays 2^-133 (subnormals); past the
+    largest finite value the result is +-inf."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                        # x = m 2^e with 0.5 <= |m| < 1
+    q = np.maximum(e - 8, -133)               # exponent of the quantum: 8 significant bits
+    y = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+    big = np.abs(y) > _BF16_MAX
+    return np.where(big, np.copysign(np.inf, x), np.where(x == 0, x, y))
+
+
 def round_store(x: np.ndarray, dtype: torch.dtype) -> np.ndarray:
-    """Round fp64 values to the cache's storage dtype (nearest-even) and back to fp64."""
-    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(dtype).to(torch.float64).numpy()
-
-
-def rerotated_keys(doc, head_dim: int, base: float, style: int, dtype: Optional[torch.dtype]):
-    """fp64 [Hkv][n][D] keys of one reused document at their actual positions."""
-    k = rope.rotate(to64(doc.k_off), doc.delta, base, style)
-    return round_store(k, dtype) if dtype is not None else k
+    """fp64 values as the cache stores them: rounded once, to nearest even, to the storage dtype, and
+    returned as fp64.  One rounding of the exact value (not fp64 -> fp32 -> bf16, which differs from it
+    just above a bf16 tie)."""
+    if dtype == torch.bfloat16:
+        return round_bf16(x)
+    if dtype == torch.float32:
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == torch.float64:
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError("storage dtype %s" % dtype)
 
 
 def _new_rows(inp, seq: int, kv_head: int):

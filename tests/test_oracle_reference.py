@@ -75,3 +75,48 @@ def test_per_head_rows_equal_whole_call():
             ob, lb = reference.prefill_rows(inp, b, h, rows)
             np.testing.assert_allclose(ob, o[cu[b] + rows, h], rtol=0, atol=1e-12)
             np.testing.assert_allclose(lb, lse[h, cu[b] + rows], rtol=0, atol=1e-12)
+
+
+def _golden_rows(name):
+    import os
+    rows = []
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", name)):
+        if line.startswith("#") or not line.strip():
+            continue
+        a, b = line.split()[:2]
+        rows.append((float.fromhex(a), math.inf if b == "inf" else float.fromhex(b)))
+    return rows
+
+
+def test_round_store_bf16_hand_worked_values():
+    """The cache's bf16 rounding: ties to even, one rounding of the exact value (the case just above a
+    tie, where fp64 -> fp32 -> bf16 would land on the even neighbour below), subnormals, overflow."""
+    rows = _golden_rows("round_bf16.txt")
+    x = np.array([r[0] for r in rows])
+    want = np.array([r[1] for r in rows])
+    got = reference.round_store(x, torch.bfloat16)
+    np.testing.assert_array_equal(got, want)
+    # the double rounding the oracle does not do, for contrast
+    dbl = torch.tensor([1.0 + 2.0 ** -8 + 2.0 ** -40], dtype=torch.float64).float().to(torch.bfloat16).double()
+    assert float(dbl[0]) == 1.0 and reference.round_store(np.array([1.0 + 2.0 ** -8 + 2.0 ** -40]),
+                                                          torch.bfloat16)[0] == 1.0 + 2.0 ** -7
+
+
+def test_round_store_bf16_equals_torch_on_fp32_values():
+    """For values an fp32 holds exactly, one rounding to bf16 is torch's fp32 -> bf16 conversion
+    (nearest even): 200k random fp32 values over the whole exponent range, including ties."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    bits = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    ties = (rng.integers(0, 2 ** 16, size=5000, dtype=np.uint32) << 16 | 0x8000).astype(np.uint32).view(np.float32)
+    f = np.concatenate([f, ties[np.isfinite(ties)]])
+    want = torch.from_numpy(f).to(torch.bfloat16).to(torch.float64).numpy()
+    got = reference.round_store(f.astype(np.float64), torch.bfloat16)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_round_store_f32_is_nearest_even():
+    x = np.array([1.0 + 2.0 ** -24, 1.0 + 3 * 2.0 ** -24, 1.0 + 2.0 ** -24 + 2.0 ** -40])
+    np.testing.assert_array_equal(reference.round_store(x, torch.float32),
+                                  [1.0, 1.0 + 2.0 ** -22, 1.0 + 2.0 ** -23])
