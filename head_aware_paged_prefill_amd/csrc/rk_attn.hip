@@ -10,28 +10,28 @@
 // Design of attn_bf16 (one work item = 256 query rows = G heads x T tokens of one KV head; eight
 // waves of 32 rows, two per SIMD):
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: keys are the M dimension, queries the N dimension, so
-//    each lane holds one query column and 16 keys per 32x32 block; a row max is in-lane max3 ops
-//    plus one v_permlane32_swap between the two half-waves.
+//    each lane holds one query column and 16 keys per 32x32 block.
 //  * K rows sit in LDS in a permuted order (bits 2 and 3 of the key index swapped) so that the S^T
 //    accumulator register i of lane half h holds key 16*(i/8) + 8*h + i%8: the eight probabilities
-//    a lane needs as the B operand of the PV product (O^T = V^T P^T) for 16-key chunk c are
-//    exactly its registers 8c..8c+7, converted to bf16 in place -- no shuffles.
+//    a lane needs as the B operand of the PV product (O^T = V^T P^T) for a 16-key chunk are exactly
+//    eight of its registers, converted to bf16 pairs in place -- no shuffles.
 //  * V pages are stored channel-major ([D][P]) so the A operand of PV (8 consecutive keys of one
 //    channel) is one 16-byte LDS read.
 //  * Tiles reach LDS by direct 16-byte buffer->LDS loads (a descriptor on the page's scalar address,
 //    32-bit lane offset), one 1 KB block per instruction; XOR swizzles of the 16-byte chunks keep the
 //    operand reads free of bank conflicts.  The buffer form matters: with the global form in flight
 //    the compiler makes every LDS operand read wait for all outstanding ones.
-//  * Operand reads run one MFMA group ahead of their products (K chunk c + 1 during chunk c, V of
-//    the first PV group during the softmax), held in place by sched_barrier(0).
-//  * Two 64-key tiles per step, double-buffered: the next step's loads are issued before this
-//    step's MFMA work; one barrier per step.  The buffer index is a compile-time constant (the step
-//    loop is unrolled by two), so operand addresses are lane registers plus immediate offsets.
-//  * Online softmax in fp32 with exp2; the running max is only raised when a new score exceeds
-//    it by more than 2^8 in the exp2 domain, so the O rescale (64 VALU ops per block) is rare.
-//    Skipping it is exact: weights up to 2^8 are represented the same way in fp32 and bf16.
-//  * Per-wave tile classes from indices: skip (no key visible to any row of the wave), full (every
-//    key visible to every row: no per-element work) or edge (per-element index compare).
+//  * A two-phase software pipeline over 32-key blocks keeps the matrix core busy while the VALU
+//    turns scores into weights: the scores of block j+1 are multiplied beside the second half of
+//    block j's exponentials, and block j's PV product beside the first half of block j+1's.  Operand
+//    reads run four products ahead, across phases.
+//  * Online softmax in fp32 with exp2, without a per-block max: weights are taken against the running
+//    max, and only a block whose weight sum exceeds 2^8 (the one case where a weight can) rescales O
+//    and recomputes its weights against its true max.  Weights up to 2^8 are represented the same
+//    way in fp32 and bf16, so this is exact.
+//  * Two 64-key tiles per LDS step, double-buffered, two barriers per step (K is consumed one block
+//    ahead of V).  Block classes come from indices: full (no per-element work) or edge (scores
+//    outside the row's visible set set to -inf in place); no mask tensor exists.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,7 +44,7 @@ namespace {
 
 constexpr int BN = kKeyTile;
 constexpr float kNegBig = -1.0e30f;
-constexpr float kRescaleSlack = 8.0f;  // log2 of the largest un-normalised weight allowed
+constexpr float kRescaleSlack = 8.0f;  // log2 of the largest un-normalised weight allowed (attn_f32)
 
 // ------------------------------------------------------------------------------------------------
 // bf16 attention
@@ -74,20 +74,36 @@ __device__ __forceinline__ int vswz(int d, int Pt) {
 }
 
 // One work item = 256 query rows; eight waves of 32 rows (one query column of S^T per lane).
-// Each step stages TPS key tiles of 64 keys (K and V) in one of two LDS buffers while the other
-// buffer's tiles are used: the loads of step s + 1 are issued before the compute of step s and one
-// barrier closes the step.  Per tile: S^T = K Q^T (16 MFMAs), the online softmax, O^T += V^T P^T
-// (16 MFMAs).
+// Each LDS step stages TPS key tiles of 64 keys (K and V) in one of two buffers.  A wave runs over
+// the 32-key blocks of the item in a two-phase software pipeline, so the matrix core always has the
+// products of one block while the VALU works on another:
+//   phase A(j): S(j+1) = K(j+1) Q^T (NC products)    beside the exponentials of the second half of S(j)
+//   phase B(j): O^T += V(j)^T P(j)^T (NC products)   beside the exponentials of the first half of S(j+1)
+// The running max is not taken per block: the exponentials use the current one, and a block whose
+// per-lane weight sum exceeds 2^8 (then, and only then, some weight may exceed 2^8) takes a rare
+// path that finds the block's true row max, rescales O and the row sum, and recomputes the block's
+// weights.  The first block of every row takes that path (the running max starts at -1e30).
+// Operand reads run RING reads ahead of their products, across phases.  K is consumed one block
+// ahead of V, so a step has two barriers: X1 before the first product that reads the next buffer
+// (then the K tiles of the step after next are issued into this buffer), X2 after the last product
+// that reads this buffer's V (then its V tiles are issued).
 // SMALLP: 8-key pages, where one 1 KB load block spans two pages.
 template <int D, bool SMALLP>
 __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
-  constexpr int NC = D / 16;                 // 16-channel chunks of the QK product
+  constexpr int NC = D / 16;                 // 16-channel chunks of the QK product = PV products per block
   constexpr int ND = D / 32;                 // 32-channel blocks of O^T
   constexpr int UNITS = BN * D * 2 / 1024;   // 1 KB load blocks per tile, for K and for V each
   constexpr int NU = UNITS / 8;              // per wave
   constexpr int KROWS_U = 512 / D;           // K rows per block
   constexpr int TPS = RK_TILES_PER_STEP;
+#ifndef RK_RING
+#define RK_RING 4
+#endif
+  constexpr int RING = RK_RING;              // operand reads in flight ahead of their products
+  constexpr int EPM = 8 / NC;                // exponentials per product slice of a phase
+  static_assert(TPS == 2, "the block pipeline assumes two tiles per step");
   static_assert(NU >= 1 && UNITS % 8 == 0, "tile does not split over the waves");
+  static_assert(NC >= RING && RING >= 2 && EPM * NC == 8, "phase slicing");
   __shared__ __attribute__((aligned(1024))) AttnBf16Smem<D, TPS> sm;
 
   const int tid = threadIdx.x;
@@ -103,8 +119,12 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
   const int L = si.kv_len;
   const int i_max = si.q_start + tok_end - 1;
   const TileRange tr = tile_range(cls, si.q_start + it.tok0, i_max, p.sink, p.window);
-  const int ntiles = tr.count();  // >= 1
-  const int nsteps = (ntiles + TPS - 1) / TPS;
+  // An odd tile count is padded with the tile after the item's last one: its keys lie past every
+  // row, so the index masks zero its weights, and its pages are held (or replaced by the fallback
+  // page below), so everything it loads is finite.  Every step then holds two tiles and the loop has
+  // no partial step (a partial last step made the compiler keep two homes for the accumulators).
+  const int ntiles = (tr.count() + 1) & ~1;
+  const int nsteps = ntiles / TPS;
   const int32_t *__restrict__ pt = p.page_ids + p.page_base[g * p.num_seqs + it.seq];
   const bf16_t *__restrict__ kpg = static_cast<const bf16_t *>(p.k_pages);
   const bf16_t *__restrict__ vpg = static_cast<const bf16_t *>(p.v_pages);
@@ -126,7 +146,7 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
   const int pos = valid ? si.q_start + tq : -1;
   const int hq = g * p.G + hh;
   const int win_lo = cls == RK_GLOBAL ? 0 : pos - p.window + 1;  // first window key of the row
-  // wave-uniform query range: scalar registers, so tile classes are scalar branches
+  // wave-uniform query range: scalar registers, so block classes are scalar branches
   const int wmin = __builtin_amdgcn_readfirstlane(wave_min(valid ? pos : INT32_MAX));
   const int wmax = __builtin_amdgcn_readfirstlane(wave_max(pos));
 
@@ -196,8 +216,8 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
     return v;
   };
   auto fix = [&](int pg) { return pg >= 0 ? pg : pg_fallback; };
-  // loads of the step's x-th tile (key tile `tile`) into slot x of buffer buf
-  auto issue_tile = [&](int tile, int buf, int x, int ids) {
+  // K (V) loads of the step's x-th tile (key tile `tile`) into slot x of buffer buf
+  auto issue_k_tile = [&](int tile, int buf, int x, int ids) {
     const int j0 = tile * BN;
     const int lane0 = x * npt;
 #pragma unroll
@@ -212,6 +232,14 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
         const char *page = reinterpret_cast<const char *>(kpg + (int64_t)pg * page_elems + ko);  // uniform
         load_lds16_buf(page, k_loff[u], page_bytes, &sm.k[buf][x][b * 512]);
       }
+    }
+  };
+  auto issue_v_tile = [&](int tile, int buf, int x, int ids) {
+    const int j0 = tile * BN;
+    const int lane0 = x * npt;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int b = wave * NU + u;
       const int vo = P > BN ? (j0 & (P - 1)) : 0;
       if constexpr (v_split) {
         const int pg = fix(__shfl(ids, lane0 + v_pi[u]));
@@ -223,10 +251,15 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
       }
     }
   };
-  auto issue_step = [&](int step, int buf, int ids) {
+  auto issue_k = [&](int step, int buf, int ids) {
 #pragma unroll
     for (int x = 0; x < TPS; ++x)
-      if (step * TPS + x < ntiles) issue_tile(tr.tile(step * TPS + x), buf, x, ids);
+      if (step * TPS + x < ntiles) issue_k_tile(tr.tile(step * TPS + x), buf, x, ids);
+  };
+  auto issue_v = [&](int step, int buf, int ids) {
+#pragma unroll
+    for (int x = 0; x < TPS; ++x)
+      if (step * TPS + x < ntiles) issue_v_tile(tr.tile(step * TPS + x), buf, x, ids);
   };
 
   f32x16 oacc[ND];
@@ -235,144 +268,228 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
   float mrun = kNegBig, lsum = 0.f;
   const float c2 = p.scale_log2;
 
-  // one 64-key tile: first key j0, operands in Kb / Vb
-  auto tile_compute = [&](const int j0, const bf16_t *Kb, const bf16_t *Vb) __attribute__((always_inline)) {
-    const bool skip = wmax < 0 || j0 > wmax ||
-                      (cls == RK_LOCAL && j0 >= p.sink && j0 + BN - 1 <= wmin - p.window);
-    const bool full = j0 + BN - 1 <= wmin &&
-                      (cls == RK_GLOBAL || j0 + BN <= p.sink || j0 > wmax - p.window);
-    if (skip) return;
-    // S^T for the tile's 64 keys (two 32-key blocks) x this wave's 32 queries
-    f32x16 s[2] = {};
-    {
-      bf16x8 ka[2][2];
+  f32x16 sc[2];      // scores of the even / odd blocks (S^T: 16 keys of one query column per lane)
+  u32x4 pk[2][2];    // their bf16 weights (bf16 pairs): the B operands of the two 16-key chunks of PV
+  float psum[2];     // the row sum of the first half of their weights (this lane's keys)
+  bf16x8 kr[RING], vr[RING];
+
+  // ---- blocks: block q (0..3) of a step sits in tile q >> 1, half q & 1 of the step's buffer.
+  // Operand reads address LDS as a lane byte offset plus an immediate: the K offsets start at the K
+  // image, the V offsets at the V image, and every buffer, tile and channel-block displacement
+  // (< 64 KB from either) is the immediate.  opaque() keeps the compiler from folding the images'
+  // base into per-buffer copies of the lane offsets.
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  typedef __attribute__((address_space(3))) bf16x8 lds_v8;
+  lds_u8 *const lds_k = (lds_u8 *)&sm.k[0][0][0];
+  lds_u8 *const lds_v = (lds_u8 *)&sm.v[0][0][0];
+  uint32_t kofs[NC], vofs[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) ka[0][kb] = *reinterpret_cast<const bf16x8 *>(Kb + k_rd[0] + 32 * kb * D);
+  for (int c = 0; c < NC; ++c) kofs[c] = opaque((uint32_t)k_rd[c] * 2);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int cur = c & 1;
-        if (c + 1 < NC) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            ka[cur ^ 1][kb] = *reinterpret_cast<const bf16x8 *>(Kb + k_rd[c + 1] + 32 * kb * D);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][kb], qf[c], s[kb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+  for (int q4 = 0; q4 < 4; ++q4) vofs[q4] = opaque((uint32_t)v_rd[q4] * 2);
+  auto first_key = [&](int s, int q) { return tr.tile(s * TPS + (q >> 1)) * BN + 32 * (q & 1); };
+  auto read_k = [&](auto bufc, auto qc, int c) {
+    constexpr int buf = decltype(bufc)::value, q = decltype(qc)::value;
+    constexpr uint32_t imm = ((buf * TPS + (q >> 1)) * BN * D + 32 * (q & 1) * D) * 2;
+    return *(lds_v8 *)(lds_k + kofs[c] + imm);
+  };
+  // V^T operand i of block q: 16-key chunk cc = i / ND, 32-channel block db = i % ND
+  auto read_v = [&](auto bufc, auto qc, int i) {
+    constexpr int buf = decltype(bufc)::value, q = decltype(qc)::value;
+    const uint32_t imm = ((buf * TPS + (q >> 1)) * BN * D + (i % ND) * 32 * BN) * 2;
+    return *(lds_v8 *)(lds_v + vofs[2 * (q & 1) + i / ND] + imm);
+  };
+  // every key of the block visible to every row of the wave: no per-element work
+  auto is_full = [&](int jb0) {
+    return jb0 + 31 <= wmin && (cls == RK_GLOBAL || jb0 + 32 <= p.sink || jb0 > wmax - p.window);
+  };
+  // key of register i of the block: jb0 + 8 hl + 16 (i / 8) + i % 8.  The visible keys of the
+  // lane's 32-key window [jb0 + 8 hl, + 32) form a bit mask (bit o: key jb0 + 8 hl + o): causal up to
+  // the row, minus the gap between the sink and the window for LOCAL heads.  Each score is then kept
+  // or set to -inf in place (in_place_mask), so the block's scores keep their registers.
+  auto mask_block = [&](f32x16 &s, int jb0) {
+    const int jb = jb0 + 8 * hl;
+    const int hi = pos - jb;  // visible: o <= hi
+    uint32_t vis = hi >= 31 ? 0xffffffffu : (hi < 0 ? 0u : (2u << hi) - 1u);
+    if (cls != RK_GLOBAL) {
+      // LOCAL: o >= win_lo - jb (window) or o < sink - jb (sink) -- clear [max(sk, 0), lo)
+      const int lo = min(max(win_lo - jb, 0), 32), sk = min(max(p.sink - jb, 0), 32);
+      const uint32_t below_lo = lo >= 32 ? 0xffffffffu : (1u << lo) - 1u;
+      const uint32_t below_sk = sk >= 32 ? 0xffffffffu : (1u << sk) - 1u;
+      vis &= ~below_lo | below_sk;
     }
-    // V operands of the first PV group, read while the softmax runs
-    bf16x8 va[2][ND];
+    in_place_mask(s, vis);
+  };
+  auto weight = [&](float s) { return fast_exp2(fmaf(s, c2, -mrun)); };
+  auto pack = [&](float a, float b) {
+    const f32x2 t = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(t, bf16x2));
+  };
+
+  // Phase A(j): S(j+1) = K(j+1) Q^T beside the second-half weights of S(j); the last RING slices read
+  // the first V operands of PV(j).  NEXT: block j+1 exists; KPRE: its first RING K operands are in kr.
+  auto phase_a = [&](auto nextc, auto kprec, auto par, auto bc, auto qc, auto bn, auto qn) -> float {
+    constexpr bool NEXT = decltype(nextc)::value, KPRE = decltype(kprec)::value;
+    constexpr int PR = decltype(par)::value;
+    if constexpr (NEXT && !KPRE) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db) va[0][db] = *reinterpret_cast<const bf16x8 *>(Vb + v_rd[0] + db * 32 * BN);
-    __builtin_amdgcn_sched_barrier(0);
-    if (!full) {
-      // key of register i of block kb: jb + 16 * (i / 8) + i % 8, jb = j0 + 32 kb + 8 hl
+      for (int c = 0; c < RING; ++c) kr[c] = read_k(bn, qn, c);
+    }
+    if constexpr (NEXT) sc[PR ^ 1] = f32x16{};
+    float sum, ev = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int jb = j0 + 32 * kb + 8 * hl;
-        const int hi = pos - jb;     // visible: off <= hi
-        const int lo = win_lo - jb;  // local: off >= lo, or off < sk
-        const int sk = p.sink - jb;
-        if (cls == RK_GLOBAL) {
+    for (int i = 0; i < NC; ++i) {
+      if (i >= NC - RING) vr[i - (NC - RING)] = read_v(bc, qc, i - (NC - RING));
+      if constexpr (NEXT) {
+        sc[PR ^ 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % RING], qf[i], sc[PR ^ 1], 0, 0, 0);
+        if (i + RING < NC) kr[i % RING] = read_k(bn, qn, i + RING);
+      }
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int off = 16 * (i >> 3) + (i & 7);
-            s[kb][i] = off <= hi ? s[kb][i] : -INFINITY;
-          }
-        } else {
+      for (int u = 0; u < EPM; ++u) {
+        const int k = i * EPM + u;
+        const float w = weight(sc[PR][8 + k]);
+        sum = k == 0 ? w : sum + w;
+        if (k & 1) pk[PR][1][k >> 1] = pack(ev, w);
+        else ev = w;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return sum;
+  };
+  // Phase B(j): O^T += V(j)^T P(j)^T beside the first-half weights of S(j+1); the last RING slices
+  // read the first K operands of block j+2 (KPRE2) from buffer b2.
+  auto phase_b = [&](auto nextc, auto kpre2c, auto par, auto bc, auto qc, auto b2, auto q2) {
+    constexpr bool NEXT = decltype(nextc)::value, KPRE2 = decltype(kpre2c)::value;
+    constexpr int PR = decltype(par)::value;
+    float sum = 0.f, ev = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int off = 16 * (i >> 3) + (i & 7);
-            s[kb][i] = (off <= hi && (off >= lo || off < sk)) ? s[kb][i] : -INFINITY;
-          }
+    for (int i = 0; i < NC; ++i) {
+      oacc[i % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % RING], __builtin_bit_cast(bf16x8, pk[PR][i / ND]),
+                                                            oacc[i % ND], 0, 0, 0);
+      if (i + RING < NC) vr[i % RING] = read_v(bc, qc, i + RING);
+      if constexpr (KPRE2) {
+        if (i >= NC - RING) kr[i - (NC - RING)] = read_k(b2, q2, i - (NC - RING));
+      }
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int u = 0; u < EPM; ++u) {
+          const int k = i * EPM + u;
+          const float w = weight(sc[PR ^ 1][k]);
+          sum = k == 0 ? w : sum + w;
+          if (k & 1) pk[PR ^ 1][0][k >> 1] = pack(ev, w);
+          else ev = w;
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float mt = s[0][0];
+    if constexpr (NEXT) psum[PR ^ 1] = sum;
+  };
+  // After phase A(j): accept block j's weights, or (rare) rescale to its true row max and redo them.
+  auto settle = [&](auto par, float sum2) {
+    constexpr int PR = decltype(par)::value;
+    float tot = psum[PR] + sum2;
+    if (__any(tot > 256.0f)) {
+      float mt = sc[PR][0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
-    mt = halves_max(mt);
-    // The running max is only raised when a score exceeds it by more than 2^8 in the exp2 domain;
-    // O and the row sum are rescaled then.
-    const float mts = mt * c2;
-    if (__any(mts > mrun + kRescaleSlack)) {
-      const float mnew = fmaxf(mrun, mts);
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sc[PR][i]);
+      const float mnew = fmaxf(mrun, halves_max(mt) * c2);
       const float alpha = fast_exp2(mrun - mnew);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < ND; ++db) in_place_scale(oacc[db], alpha);
       lsum *= alpha;
       mrun = mnew;
-    }
-    // bf16 weights; pk[kb][cc] is the B operand of the PV product for keys 32 kb + 16 cc .. + 15
-    bf16x8 pk[2][2];
-    float ps = 0.f;
+      tot = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x8 e0, e1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        e0[i] = fast_exp2(fmaf(s[kb][i], c2, -mrun));
-        e1[i] = fast_exp2(fmaf(s[kb][i + 8], c2, -mrun));
-        ps += e0[i] + e1[i];
+      for (int i = 0; i < 8; i += 2) {
+        const float w0 = weight(sc[PR][i]), w1 = weight(sc[PR][i + 1]);
+        const float w2 = weight(sc[PR][8 + i]), w3 = weight(sc[PR][9 + i]);
+        tot += (w0 + w1) + (w2 + w3);
+        pk[PR][0][i >> 1] = pack(w0, w1);
+        pk[PR][1][i >> 1] = pack(w2, w3);
       }
-      pk[kb][0] = __builtin_convertvector(e0, bf16x8);
-      pk[kb][1] = __builtin_convertvector(e1, bf16x8);
     }
-    lsum += ps;
-    // O^T += V^T P^T
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int cur = g4 & 1;
-      if (g4 + 1 < 4) {
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-          va[cur ^ 1][db] = *reinterpret_cast<const bf16x8 *>(Vb + v_rd[g4 + 1] + db * 32 * BN);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cur][db], pk[g4 >> 1][g4 & 1], oacc[db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    lsum += tot;
   };
 
-  // Loads retire in issue order.  Order per step: data of the next step, then the page ids of the
-  // step after it; at the end of the step the next step's data must be in LDS and only the id load
-  // (when one was issued) may still be in flight.
-  constexpr int WAIT_ALL = 0x0f70;      // vmcnt(0)
-  constexpr int WAIT_BUT_ONE = 0x0f71;  // vmcnt(1)
+  // Loads retire in issue order.  Prologue: step 0, then (after the barrier) step 1 and the page ids
+  // of step 2; X1 of every step waits for everything issued so far.
   int ids = load_ids(0);
-  issue_step(0, 0, ids);
-  bool ids_pending = nsteps > 1;
-  if (ids_pending) ids = load_ids(1);
-  if (ids_pending) __builtin_amdgcn_s_waitcnt(WAIT_BUT_ONE);
-  else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+  issue_k(0, 0, ids);
+  issue_v(0, 0, ids);
+  if (nsteps > 1) ids = load_ids(1);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
-
-  // One step.  The LDS buffer index is a template constant (the loop below is unrolled by two),
-  // so every operand address is a lane register plus an immediate offset.
-  auto step = [&](const int s, auto bufc) __attribute__((always_inline)) {
-    constexpr int buf = decltype(bufc)::value;
-    ids_pending = false;
-    if (s + 1 < nsteps) {
-      issue_step(s + 1, buf ^ 1, ids);
-      ids_pending = s + 2 < nsteps;
-      if (ids_pending) ids = load_ids(s + 2);
+  if (nsteps > 1) {
+    issue_k(1, 1, ids);
+    issue_v(1, 1, ids);
+    if (nsteps > 2) ids = load_ids(2);
+  }
+  // block 0: its scores alone, then the first half of its weights
+  {
+    sc[0] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < RING; ++c) kr[c] = read_k(IntC<0>{}, IntC<0>{}, c);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % RING], qf[i], sc[0], 0, 0, 0);
+      if (i + RING < NC) kr[i % RING] = read_k(IntC<0>{}, IntC<0>{}, i + RING);
     }
 #pragma unroll
-    for (int x = 0; x < TPS; ++x)
-      if (s * TPS + x < ntiles) tile_compute(tr.tile(s * TPS + x) * BN, sm.k[buf][x], sm.v[buf][x]);
-    if (ids_pending) __builtin_amdgcn_s_waitcnt(WAIT_BUT_ONE);
-    else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
-    __syncthreads();
+    for (int c = 0; c < RING; ++c) kr[c] = read_k(IntC<0>{}, IntC<1>{}, c);
+    const int jb0 = first_key(0, 0);
+    if (!is_full(jb0)) mask_block(sc[0], jb0);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float w0 = weight(sc[0][i]), w1 = weight(sc[0][i + 1]);
+      sum += w0 + w1;
+      pk[0][0][i >> 1] = pack(w0, w1);
+    }
+    psum[0] = sum;
+  }
+
+  const IntC<0> c0{};
+  const IntC<1> c1{};
+  const IntC<2> c2i{};
+  const IntC<3> c3i{};
+  const IntC<true> yes{};
+  const IntC<false> no{};
+  // One step: blocks 0..3 of buffer b.  After the item's last block the pipeline still runs the
+  // scores of one more block, on whatever the other buffer holds (in bounds, no load in flight into
+  // it), and never uses them: NC products per item instead of a second copy of the pipeline's tail.
+  auto step = [&](const int s, auto bufc) __attribute__((always_inline)) {
+    constexpr int b = decltype(bufc)::value;
+    const IntC<b ^ 1> bn{};
+    const bool last = s + 1 >= nsteps;
+    settle(c0, phase_a(yes, yes, c0, bufc, c0, bufc, c1));
+    if (!is_full(first_key(s, 1))) mask_block(sc[1], first_key(s, 1));
+    phase_b(yes, yes, c0, bufc, c0, bufc, c2i);
+    settle(c1, phase_a(yes, yes, c1, bufc, c1, bufc, c2i));
+    if (!is_full(first_key(s, 2))) mask_block(sc[0], first_key(s, 2));
+    phase_b(yes, yes, c1, bufc, c1, bufc, c3i);
+    settle(c0, phase_a(yes, yes, c0, bufc, c2i, bufc, c3i));
+    if (!is_full(first_key(s, 3))) mask_block(sc[1], first_key(s, 3));
+    phase_b(yes, no, c0, bufc, c2i, bufc, c0);
+    // X1: the next step's tiles are in LDS and every wave is done with this buffer's K
+    if (!last) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      __syncthreads();
+      if (s + 2 < nsteps) issue_k(s + 2, b, ids);
+    }
+    // block 3; its successor is block 0 of the next step
+    settle(c1, phase_a(yes, no, c1, bufc, c3i, bn, c0));
+    if (!last && !is_full(first_key(s + 1, 0))) mask_block(sc[0], first_key(s + 1, 0));
+    phase_b(yes, yes, c1, bufc, c3i, bn, c1);
+    // X2: every wave is done with this buffer's V
+    if (s + 2 < nsteps) {
+      __syncthreads();
+      issue_v(s + 2, b, ids);
+      if (s + 3 < nsteps) ids = load_ids(s + 3);
+    }
   };
   for (int s = 0; s < nsteps; s += 2) {
-    step(s, IntC<0>{});
-    if (s + 1 < nsteps) step(s + 1, IntC<1>{});
+    step(s, c0);
+    if (s + 1 < nsteps) step(s + 1, c1);
   }
 
   // ---- epilogue: O^T accumulator (lane column = query, 16 channels per 32-channel block)

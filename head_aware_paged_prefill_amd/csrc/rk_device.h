@@ -11,6 +11,8 @@ namespace rk {
 typedef __bf16 bf16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -79,6 +81,43 @@ __device__ __forceinline__ void load_lds16_buf(const void *base, uint32_t voff, 
 __device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_block) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gsrc,
                                    (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
+}
+
+
+// In-place updates of a 16-register accumulator tuple.  Written as inline asm with tied operands so
+// the tuple keeps its registers (a compiler-generated select or multiply may write a fresh tuple and
+// copy it back).  The values come from matrix products, which the hardware does not interlock with
+// VALU reads: the leading s_nops give the wait states an 8-pass product needs before its result is
+// read, whatever came between.
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory"); }
+
+// s[i] = bit o(i) of vis ? s[i] : -inf, o(i) = 16 (i / 8) + i % 8 (the key offset of register i)
+__device__ __forceinline__ void in_place_mask(f32x16 &s, uint32_t vis) {
+  mfma_result_wait();
+  const float ninf = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = s[i];
+    uint32_t t;
+    asm volatile("v_bfe_i32 %1, %2, %3, 1\n\tv_bfi_b32 %0, %1, %0, %4"
+                 : "+v"(x), "=&v"(t)
+                 : "v"(vis), "i"(16 * (i >> 3) + (i & 7)), "v"(ninf));
+    s[i] = x;
+  }
+}
+
+// v *= a for every element, in place
+__device__ __forceinline__ void in_place_scale(f32x16 &v, float a) {
+  mfma_result_wait();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = v[i];
+    asm volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(a));
+    v[i] = x;
+  }
+  // the tuple is the accumulator of later products: wait states between a VALU write and a
+  // matrix product reading it (the compiler does not see the writes inside the asm)
+  asm volatile("s_nop 4" ::: "memory");
 }
 
 }  // namespace rk
