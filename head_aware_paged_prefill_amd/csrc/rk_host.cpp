@@ -1245,8 +1245,11 @@ rk_status rk_seg_attn_decode(rk_pool *pool, const rk_tables *t, int32_t layer, c
   if (!q || !o || !aligned16(q) || !aligned16(o)) return fail(RK_ERR_INVALID_ARG, "q / o null or not 16-byte aligned");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(RK_ERR_INVALID_ARG, "lse not 4-byte aligned");
   if (!(softmax_scale <= 0.0f) && !std::isfinite(softmax_scale)) return fail(RK_ERR_INVALID_ARG, "softmax_scale not finite");
-  st = append_impl(pool, t, layer, k_new, v_new, stream);
-  if (st != RK_OK) return st;
+  // both NULL: the caller appended the tokens already (rk_seg_append_kv); one NULL is an error
+  if (k_new || v_new) {
+    st = append_impl(pool, t, layer, k_new, v_new, stream);
+    if (st != RK_OK) return st;
+  }
   const int32_t li = layer - t->layer_begin;
   const rk_tables::LayerDev &d = t->dev[li];
   rk::DecodeParams p{};

@@ -376,10 +376,13 @@ __global__ void __launch_bounds__(256) fill_zero(float *x, int64_t n) {
 }  // namespace
 
 hipError_t launch_key_mass(const MassParams &p, int head_dim, hipStream_t stream) {
-  if (p.n_units <= 0) return hipSuccess;
+  // every output entry is written: zero first (keys no query sees, also when the call has no query
+  // row at all), then the units add their partial sums
   const int64_t n_out = (int64_t)p.H * p.total_kv;
-  hipLaunchKernelGGL(fill_zero, dim3((unsigned)std::min<int64_t>((n_out + 255) / 256, 1 << 16)), dim3(256), 0, stream,
-                     p.mass, n_out);
+  if (n_out > 0)
+    hipLaunchKernelGGL(fill_zero, dim3((unsigned)std::min<int64_t>((n_out + 255) / 256, 1 << 16)), dim3(256), 0, stream,
+                       p.mass, n_out);
+  if (p.n_units <= 0) return hipGetLastError();
   const dim3 grid((unsigned)p.n_units);
   const bool wide = mass_keys_per_wave(p.G) == 64;
   if (head_dim == 128) {

@@ -158,9 +158,19 @@ typedef struct {
 
 /* -- pool ---------------------------------------------------------------------------------- */
 
-/* Create a pool over caller-owned page storage.  Host only: no device work.
+/* Create a pool over caller-owned page storage: the KV pools that BUILDSTATE prepares and
+ * SELECTVISIBLESTATE draws a request's pages from (page "RedKnot - Xiaohongshuが開発したオープン
+ * ソースの長文テキスト推論高速化エンジン" (aiboss88.com), section RedKnotの使い方, BUILDSTATE item;
+ * the pages' separate global and local pools are one physical pool here, a page's owner fixing its
+ * class).  Host only: no device work.  desc: every field is read at creation and copied; the page
+ * storage stays the caller's and must outlive the pool.
  * Storage assumption: page p of the K array starts at k_pages + p*page_size*head_dim elements,
- * of the V array at v_pages + p*head_dim*page_size elements.  Errors: RK_ERR_INVALID_ARG. */
+ * of the V array at v_pages + p*head_dim*page_size elements.  initial_free_order (optional) is a
+ * permutation of [0, num_pages): the free list, head first.
+ * Errors: RK_ERR_INVALID_ARG (null desc or out, num_layers or num_kv_heads < 1, num_pages outside
+ * [0, 2^31), null page arrays with num_pages > 0, page arrays not 16-byte aligned, initial_free_order
+ * not a permutation); RK_ERR_UNSUPPORTED (head_dim not 64 / 128, page_size not a power of two in
+ * [8, 256], unknown dtype).  *out is untouched on error. */
 rk_status rk_seg_pool_create(const rk_pool_desc *desc, rk_pool **out);
 
 /* Destroy a pool.  Fails with RK_ERR_STATE while tables built from it are alive. */

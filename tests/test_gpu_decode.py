@@ -170,3 +170,39 @@ def test_decode_rejects_unsupported_and_prefill_shaped_tables():
             assert ei.value.status == rk_seg.RK_ERR_STATE
     finally:
         r.close()
+
+
+def test_decode_with_null_kv_after_explicit_append_is_bit_identical():
+    """rk_seg_attn_decode with k_new = v_new = NULL skips the append: after rk_seg_append_kv of the same
+    tokens it returns the bits of the call that appends them itself."""
+    wl = workloads.random_small(11, torch.bfloat16, allow_reuse=False)
+    say("decode NULL k/v: kv_lens=%s G=%d" % (wl.kv_lens, wl.group))
+    B = wl.num_seqs
+    inp = workloads.make_inputs(wl, num_pages=workloads.pool_pages_needed_hint(wl) + wl.pool_slack + 4 * B * wl.num_kv_heads)
+    dinp = to_dev(inp)
+    outs = []
+    for explicit in (False, True):
+        r = PrefillRunner(wl, free_order=inp.free_order, poison=True)
+        try:
+            r.build()
+            r.attend(dinp.q, dinp.k_new, dinp.v_new)
+            r.trim()
+            r.advance([1] * B)
+            q, k, v = workloads.decode_inputs(wl, 0, B)
+            q, k, v = q.cuda(), k.cuda(), v.cuda()
+            o = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=wl.dtype, device="cuda")
+            lse = torch.empty((wl.num_q_heads, B), dtype=torch.float32, device="cuda")
+            if explicit:
+                rk_seg.rk_seg_append_kv(r.tables, wl.layer, k, v)
+                rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, None, None, o, lse)
+            else:
+                rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, k, v, o, lse)
+            torch.cuda.synchronize()
+            outs.append((o.cpu(), lse.cpu()))
+            with pytest.raises(rk_seg.RkError) as ei:  # one of the two missing is an error
+                rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, k, None, o, lse)
+            assert ei.value.status == rk_seg.RK_ERR_INVALID_ARG
+        finally:
+            r.close()
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])

@@ -172,3 +172,22 @@ def test_qwen32b_mass_sampled():
 
 def test_dsv4flash_split_mass_sampled():
     _sampled_full(workloads.dsv4flash_split(3), "DeepSeek-V4-Flash-style EXECUTE split mass")
+
+
+def test_mass_with_no_query_rows_writes_zeros():
+    """A call whose sequences have keys but no query row (q_start = kv_len): every mass entry is
+    written, and each is 0 (no query sees any key).  The output starts as a sentinel."""
+    wl = workloads.Workload(name="mass without queries", config_id=431, num_layers=1, layer=0,
+                            kv_lens=[300, 77], q_starts=[300, 77], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                            page_size=16, sink=4, window=64, dtype=torch.bfloat16,
+                            head_class=np.array([[1, 0]], np.uint8), pool_slack=3)
+    say(wl.name)
+    r = PrefillRunner(wl, num_pages=workloads.pool_pages_needed_hint(wl) + 8)
+    try:
+        r.build()
+        mass = torch.full((wl.num_q_heads, sum(wl.kv_lens)), 7.0, dtype=torch.float32, device="cuda")
+        rk_seg.rk_seg_key_mass(r.tables, wl.layer, None, None, mass)
+        torch.cuda.synchronize()
+        assert torch.equal(mass, torch.zeros_like(mass))
+    finally:
+        r.close()
