@@ -13,7 +13,9 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librk_seg.so")
+# RK_SEG_LIB selects another build of the same library, e.g. the sanitizer build
+# (`python -m head_aware_paged_prefill_amd.build --checked` -> librk_seg_checked.so)
+LIB_PATH = os.environ.get("RK_SEG_LIB") or os.path.join(_HERE, "librk_seg.so")
 
 RK_OK = 0
 RK_ERR_INVALID_ARG = -1
