@@ -67,6 +67,7 @@ template <int D, int TPS>
 struct AttnBf16Smem {
   bf16_t k[2][TPS][BN * D];  // double buffer: the next step's tiles load while these are used
   bf16_t v[2][TPS][D * BN];
+  int32_t ids[8][2][64];     // per wave: the page ids of the next steps into buffer 0 / 1
 };
 
 __device__ __forceinline__ int vswz(int d, int Pt) {
@@ -84,9 +85,11 @@ __device__ __forceinline__ int vswz(int d, int Pt) {
 // path that finds the block's true row max, rescales O and the row sum, and recomputes the block's
 // weights.  The first block of every row takes that path (the running max starts at -1e30).
 // Operand reads run RING reads ahead of their products, across phases.  K is consumed one block
-// ahead of V, so a step has two barriers: X1 before the first product that reads the next buffer
-// (then the K tiles of the step after next are issued into this buffer), X2 after the last product
-// that reads this buffer's V (then its V tiles are issued).
+// ahead of V, so a step has two barriers: X1 before the first product that reads the next buffer's
+// K (then the K tiles of the step after next are issued into this buffer), X2 before the first
+// product that reads the next buffer's V (then this buffer's V tiles are issued).  Each waits for
+// exactly the loads the following blocks need, so the step after next stays in flight: K and V
+// both get a whole step of lead.
 // SMALLP: 8-key pages, where one 1 KB load block spans two pages.
 template <int D, bool SMALLP>
 __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
@@ -201,53 +204,58 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) k_rd[c] = m * D + (((2 * c + hl) ^ kswz<D>(m)) << 3);
 
-  // Page ids of a step's tiles: one vector load per wave (lane x * npt + i holds the id of page i
-  // of the step's x-th tile), issued a step ahead and read back with readlane, so the lookup latency
-  // stays off the critical path and no scalar load shares the LDS wait counter with operand reads.
+  // Page ids of a step's tiles: one direct 4-byte-per-lane load per wave into the wave's LDS slot
+  // of that step's buffer (lane x * npt + i: the id of page i of the step's x-th tile), issued a step
+  // ahead and read back with one LDS read after the step's first barrier.  A vector-register result
+  // would make the compiler wait for every load in flight before its first use; the LDS slot is
+  // covered by the step's own wait.  Lanes past the step's pages, and pages past the sequence, read
+  // the last logical page (held: it holds kv_len - 1), so every id is a held page or -1.
   const int npt = P < BN ? BN / P : 1;
-  auto load_ids = [&](int step) -> int {
-    const int x = lane / npt, i = lane - x * npt;
-    const int t = step * TPS + x;
-    int v = -1;
-    if (x < TPS && t < ntiles) {
-      const int lp = ((tr.tile(t) * BN) >> log2P) + i;
-      if (lp < n_logical) v = pt[lp];
-    }
-    return v;
+  auto issue_ids = [&](int step, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
+    const int x = min(lane / npt, TPS - 1), i = lane % npt;
+    const int lp = min(((tr.tile(step * TPS + x) * BN) >> log2P) + i, n_logical - 1);
+    load_lds4_buf(pt, (uint32_t)lp * 4u, (uint32_t)n_logical * 4u, &sm.ids[wave][slot][0]);
   };
-  auto fix = [&](int pg) { return pg >= 0 ? pg : pg_fallback; };
+  // the ids with the fallback page in place of -1 (one select per step instead of one per load)
+  auto read_ids = [&](auto slotc) -> int {
+    constexpr int slot = decltype(slotc)::value;
+    const int v = sm.ids[wave][slot][lane];
+    return v >= 0 ? v : pg_fallback;
+  };
+  // Byte address of a byte offset within physical page pg: ids are non-negative, so the page offset
+  // is one unsigned 32 x 32 -> 64-bit product (two scalar instructions per load).
+  auto page_at = [&](const bf16_t *pool, int pg, uint32_t off) {
+    return reinterpret_cast<const char *>(pool) + ((uint64_t)(uint32_t)pg * page_bytes + off);
+  };
   // K (V) loads of the step's x-th tile (key tile `tile`) into slot x of buffer buf
   auto issue_k_tile = [&](int tile, int buf, int x, int ids) {
-    const int j0 = tile * BN;
     const int lane0 = x * npt;
+    const uint32_t ko = P > BN ? (uint32_t)((tile * BN) & (P - 1)) * D * 2 : 0u;  // tiles within a large page
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int b = wave * NU + u;
-      const int ko = P > BN ? (j0 & (P - 1)) * D : 0;
       if constexpr (k_split) {
-        const int pg = fix(__shfl(ids, lane0 + (swap_bits23(b * KROWS_U + lane / (D / 8)) >> log2P)));
-        load_lds16(reinterpret_cast<const char *>(kpg + (int64_t)pg * page_elems + ko) + k_loff[u], &sm.k[buf][x][b * 512]);
+        const int pg = __shfl(ids, lane0 + (swap_bits23(b * KROWS_U + lane / (D / 8)) >> log2P));
+        load_lds16(page_at(kpg, pg, ko) + k_loff[u], &sm.k[buf][x][b * 512]);
       } else {
-        const int pg = fix(__builtin_amdgcn_readlane(ids, lane0 + (P < BN ? (k_key0[u] >> log2P) : 0)));
-        const char *page = reinterpret_cast<const char *>(kpg + (int64_t)pg * page_elems + ko);  // uniform
-        load_lds16_buf(page, k_loff[u], page_bytes, &sm.k[buf][x][b * 512]);
+        const int pg = __builtin_amdgcn_readlane(ids, lane0 + (P < BN ? (k_key0[u] >> log2P) : 0));
+        load_lds16_buf(page_at(kpg, pg, ko), k_loff[u], page_bytes, &sm.k[buf][x][b * 512]);
       }
     }
   };
   auto issue_v_tile = [&](int tile, int buf, int x, int ids) {
-    const int j0 = tile * BN;
     const int lane0 = x * npt;
+    const uint32_t vo = P > BN ? (uint32_t)((tile * BN) & (P - 1)) * 2 : 0u;  // key offset within a large page
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int b = wave * NU + u;
-      const int vo = P > BN ? (j0 & (P - 1)) : 0;
       if constexpr (v_split) {
-        const int pg = fix(__shfl(ids, lane0 + v_pi[u]));
-        load_lds16(reinterpret_cast<const char *>(vpg + (int64_t)pg * page_elems + vo) + v_loff[u], &sm.v[buf][x][b * 512]);
+        const int pg = __shfl(ids, lane0 + v_pi[u]);
+        load_lds16(page_at(vpg, pg, vo) + v_loff[u], &sm.v[buf][x][b * 512]);
       } else {
-        const int pg = fix(__builtin_amdgcn_readlane(ids, lane0 + v_pi[u]));
-        const char *page = reinterpret_cast<const char *>(vpg + (int64_t)pg * page_elems + vo);  // uniform
-        load_lds16_buf(page, v_loff[u], page_bytes, &sm.v[buf][x][b * 512]);
+        const int pg = __builtin_amdgcn_readlane(ids, lane0 + v_pi[u]);
+        load_lds16_buf(page_at(vpg, pg, vo), v_loff[u], page_bytes, &sm.v[buf][x][b * 512]);
       }
     }
   };
@@ -411,18 +419,23 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
     lsum += tot;
   };
 
-  // Loads retire in issue order.  Prologue: step 0, then (after the barrier) step 1 and the page ids
-  // of step 2; X1 of every step waits for everything issued so far.
-  int ids = load_ids(0);
-  issue_k(0, 0, ids);
-  issue_v(0, 0, ids);
-  if (nsteps > 1) ids = load_ids(1);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  // Loads retire in issue order.  Prologue: the ids and tiles of step 0; after the barrier K(1),
+  // the ids of step 2, V(1).  Then X1 of step s issues K(s + 2), X2 the ids of step s + 3 and
+  // V(s + 2): every wait below names exactly the loads that may stay in flight.
+  constexpr int NLD = NU * TPS;  // loads of one step's K (or V) per wave
+  issue_ids(0, IntC<0>{});
+  wait_vmcnt<0>();
+  int idv = read_ids(IntC<0>{});
+  issue_k(0, 0, idv);
+  issue_v(0, 0, idv);
+  if (nsteps > 1) issue_ids(1, IntC<1>{});
+  wait_vmcnt<0>();
   __syncthreads();
   if (nsteps > 1) {
-    issue_k(1, 1, ids);
-    issue_v(1, 1, ids);
-    if (nsteps > 2) ids = load_ids(2);
+    idv = read_ids(IntC<1>{});
+    issue_k(1, 1, idv);
+    if (nsteps > 2) issue_ids(2, IntC<0>{});
+    issue_v(1, 1, idv);
   }
   // block 0: its scores alone, then the first half of its weights
   {
@@ -470,21 +483,28 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
     settle(c0, phase_a(yes, yes, c0, bufc, c2i, bufc, c3i));
     if (!is_full(first_key(s, 3))) mask_block(sc[1], first_key(s, 3));
     phase_b(yes, no, c0, bufc, c2i, bufc, c0);
-    // X1: the next step's tiles are in LDS and every wave is done with this buffer's K
+    // X1: the next step's K is in LDS and every wave is done with this buffer's K.  In flight after
+    // K(s + 1) and the ids of step s + 2: V(s + 1).
     if (!last) {
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-      __syncthreads();
-      if (s + 2 < nsteps) issue_k(s + 2, b, ids);
+      wait_vmcnt<NLD>();
+      lds_barrier();
+      idv = read_ids(bufc);
+      if (s + 2 < nsteps) issue_k(s + 2, b, idv);
     }
     // block 3; its successor is block 0 of the next step
     settle(c1, phase_a(yes, no, c1, bufc, c3i, bn, c0));
     if (!last && !is_full(first_key(s + 1, 0))) mask_block(sc[0], first_key(s + 1, 0));
     phase_b(yes, yes, c1, bufc, c3i, bn, c1);
-    // X2: every wave is done with this buffer's V
-    if (s + 2 < nsteps) {
-      __syncthreads();
-      issue_v(s + 2, b, ids);
-      if (s + 3 < nsteps) ids = load_ids(s + 3);
+    // X2: the next step's V is in LDS and every wave is done with this buffer's V.  In flight after
+    // V(s + 1): K(s + 2), when it exists.
+    if (!last) {
+      if (s + 2 < nsteps) wait_vmcnt<NLD>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (s + 2 < nsteps) {
+        if (s + 3 < nsteps) issue_ids(s + 3, bn);
+        issue_v(s + 2, b, idv);
+      }
     }
   };
   for (int s = 0; s < nsteps; s += 2) {

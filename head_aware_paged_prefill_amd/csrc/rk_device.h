@@ -84,6 +84,31 @@ __device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_block) {
 }
 
 
+// vmcnt(N): wait until at most N vector memory operations of this wave are outstanding (they retire
+// in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// A workgroup barrier without __syncthreads()'s memory fences.  Those make the compiler wait for
+// every outstanding load into LDS (vmcnt(0)), also the tiles of later steps still in flight; the
+// caller waits for exactly the loads it needs first (wait_vmcnt).  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 4 bytes per lane from base + a 32-bit lane offset into a dense 256-byte LDS block (lane l writes
+// bytes 4 l .. 4 l + 3), buffer form with range `bytes`
+__device__ __forceinline__ void load_lds4_buf(const void *base, uint32_t voff, uint32_t bytes, void *lds_block) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_block, 4, voff, 0, 0, 0);
+}
+
 // In-place updates of a 16-register accumulator tuple.  Written as inline asm with tied operands so
 // the tuple keeps its registers (a compiler-generated select or multiply may write a fresh tuple and
 // copy it back).  The values come from matrix products, which the hardware does not interlock with
