@@ -113,53 +113,81 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
   // the wave index is uniform: keep it (and everything derived from it) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hl = lane >> 5, m = lane & 31;
-  const Item it = p.items[blockIdx.x];
-  if (it.seq < 0) return;  // schedule padding: keeps the next items on their XCD
-  const SeqInfo si = p.seqs[it.seq];
-  const int g = it.kv_head;
-  const int cls = p.head_class[g];
-  const int tok_end = min(it.tok0 + p.T, si.n_q);
-  const int L = si.kv_len;
-  const int i_max = si.q_start + tok_end - 1;
-  const TileRange tr = tile_range(cls, si.q_start + it.tok0, i_max, p.sink, p.window);
+  const ItemCtx ic = p.ictx[blockIdx.x];
+  if (ic.kvh_cls < 0) return;  // schedule padding: keeps the next items on their XCD
+  const int g = ic.kvh_cls & 0xffff;
+  const int cls = ic.kvh_cls >> 16;
+  const int tok_end = min(ic.tok0 + p.T, ic.n_q);
+  const int L = ic.kv_len;
+  const int i_max = ic.q_start + tok_end - 1;
+  const TileRange tr = tile_range(cls, ic.q_start + ic.tok0, i_max, p.sink, p.window);
   // An odd tile count is padded with the tile after the item's last one: its keys lie past every
   // row, so the index masks zero its weights, and its pages are held (or replaced by the fallback
   // page below), so everything it loads is finite.  Every step then holds two tiles and the loop has
   // no partial step (a partial last step made the compiler keep two homes for the accumulators).
   const int ntiles = (tr.count() + 1) & ~1;
   const int nsteps = ntiles / TPS;
-  const int32_t *__restrict__ pt = p.page_ids + p.page_base[g * p.num_seqs + it.seq];
+  const int32_t *__restrict__ pt = p.page_ids + ic.page_off;
   const bf16_t *__restrict__ kpg = static_cast<const bf16_t *>(p.k_pages);
   const bf16_t *__restrict__ vpg = static_cast<const bf16_t *>(p.v_pages);
   const int P = p.P, log2P = p.log2P;
   const int Pt = P < BN ? P : BN;
   const int n_logical = (L + P - 1) >> log2P;
-  const int64_t page_elems = (int64_t)P * D;
-  const uint32_t page_bytes = (uint32_t)page_elems * 2;
+  const uint32_t page_bytes = (uint32_t)(P * D * 2);
   // Pages a tile touches but the head does not hold (or past the sequence's last page) are read
   // from this page instead: the page of the item's last query, held and fully written (the append
   // clears its slots past kv_len).  Its keys are masked out, so only finiteness matters.
-  const int pg_fallback = pt[i_max >> log2P];
+  const int pg_fallback = ic.fallback;
 
   // ---- the query row (column of S^T) this lane owns
   const int r = wave * 32 + m;
   const int hh = r / p.T;
-  const int tq = it.tok0 + (r - hh * p.T);
+  const int tq = ic.tok0 + (r - hh * p.T);
   const bool valid = hh < p.G && tq < tok_end;
-  const int pos = valid ? si.q_start + tq : -1;
+  const int pos = valid ? ic.q_start + tq : -1;
   const int hq = g * p.G + hh;
   const int win_lo = cls == RK_GLOBAL ? 0 : pos - p.window + 1;  // first window key of the row
-  // wave-uniform query range: scalar registers, so block classes are scalar branches
-  const int wmin = __builtin_amdgcn_readfirstlane(wave_min(valid ? pos : INT32_MAX));
-  const int wmax = __builtin_amdgcn_readfirstlane(wave_max(pos));
+  // Wave-uniform query range, in scalar registers, so block classes are scalar branches.  When T is a
+  // multiple of 32 (G in {1, 2, 4, 8}) the wave's rows are 32 consecutive tokens of one head and the
+  // range is exact; otherwise the item's range, which contains the wave's rows (block classes only
+  // decide whether a block is masked, so a wider range costs masking work, never correctness).
+  int wmin, wmax;
+  if ((p.T & 31) == 0) {
+    const int t0 = ic.tok0 + (wave * 32) % p.T;
+    wmin = t0 < tok_end ? ic.q_start + t0 : INT32_MAX;
+    wmax = t0 < tok_end ? ic.q_start + min(t0 + 31, tok_end - 1) : -1;
+  } else {
+    wmin = ic.q_start + ic.tok0;
+    wmax = i_max;
+  }
 
   bf16x8 qf[NC];
+
+  // Page ids of a step's tiles: one direct 4-byte-per-lane load per wave into the wave's LDS slot
+  // of that step's buffer (lane x * npt + i: the id of page i of the step's x-th tile), issued a step
+  // ahead and read back with one LDS read after the step's first barrier.  A vector-register result
+  // would make the compiler wait for every load in flight before its first use; the LDS slot is
+  // covered by the step's own wait.  Lanes past the step's pages, and pages past the sequence, read
+  // the last logical page (held: it holds kv_len - 1), so every id is a held page or -1.
+  const int npt = P < BN ? BN / P : 1;
+  auto issue_ids = [&](int step, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
+    const int x = min(lane / npt, TPS - 1), i = lane % npt;
+    const int lp = min(((tr.tile(step * TPS + x) * BN) >> log2P) + i, n_logical - 1);
+    load_lds4_buf(pt, (uint32_t)lp * 4u, (uint32_t)n_logical * 4u, &sm.ids[wave][slot][0]);
+  };
+  // the first step's ids and the queries load while the tile geometry below is computed
+  issue_ids(0, IntC<0>{});
+  asm volatile("" ::: "memory");  // the query loads below stay behind the ids load
   {
-    const bf16_t *qrow = static_cast<const bf16_t *>(p.q) + ((int64_t)(si.cu_q + tq) * p.H + hq) * D;
+    // every lane loads (rows outside the item read the item's first row and are zeroed), so exactly
+    // NC query loads follow the ids load
+    const int tq_c = valid ? tq : ic.tok0, hq_c = valid ? hq : g * p.G;
+    const bf16_t *qrow = static_cast<const bf16_t *>(p.q) + ((int64_t)(ic.cu_q + tq_c) * p.H + hq_c) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      bf16x8 z = {};
-      qf[c] = valid ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * c + 8 * hl) : z;
+      const bf16x8 z = {}, v = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c + 8 * hl);
+      qf[c] = valid ? v : z;
     }
   }
 
@@ -204,19 +232,6 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) k_rd[c] = m * D + (((2 * c + hl) ^ kswz<D>(m)) << 3);
 
-  // Page ids of a step's tiles: one direct 4-byte-per-lane load per wave into the wave's LDS slot
-  // of that step's buffer (lane x * npt + i: the id of page i of the step's x-th tile), issued a step
-  // ahead and read back with one LDS read after the step's first barrier.  A vector-register result
-  // would make the compiler wait for every load in flight before its first use; the LDS slot is
-  // covered by the step's own wait.  Lanes past the step's pages, and pages past the sequence, read
-  // the last logical page (held: it holds kv_len - 1), so every id is a held page or -1.
-  const int npt = P < BN ? BN / P : 1;
-  auto issue_ids = [&](int step, auto slotc) {
-    constexpr int slot = decltype(slotc)::value;
-    const int x = min(lane / npt, TPS - 1), i = lane % npt;
-    const int lp = min(((tr.tile(step * TPS + x) * BN) >> log2P) + i, n_logical - 1);
-    load_lds4_buf(pt, (uint32_t)lp * 4u, (uint32_t)n_logical * 4u, &sm.ids[wave][slot][0]);
-  };
   // the ids with the fallback page in place of -1 (one select per step instead of one per load)
   auto read_ids = [&](auto slotc) -> int {
     constexpr int slot = decltype(slotc)::value;
@@ -423,8 +438,7 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
   // the ids of step 2, V(1).  Then X1 of step s issues K(s + 2), X2 the ids of step s + 3 and
   // V(s + 2): every wait below names exactly the loads that may stay in flight.
   constexpr int NLD = NU * TPS;  // loads of one step's K (or V) per wave
-  issue_ids(0, IntC<0>{});
-  wait_vmcnt<0>();
+  wait_vmcnt<NC>();  // the ids; the queries may still be in flight
   int idv = read_ids(IntC<0>{});
   issue_k(0, 0, idv);
   issue_v(0, 0, idv);
@@ -516,7 +530,7 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
   const float lt = halves_sum(lsum);
   if (!valid) return;
   const float inv = 1.0f / lt;
-  bf16_t *orow = static_cast<bf16_t *>(p.o) + ((int64_t)(si.cu_q + tq) * p.H + hq) * D;
+  bf16_t *orow = static_cast<bf16_t *>(p.o) + ((int64_t)(ic.cu_q + tq) * p.H + hq) * D;
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -526,7 +540,7 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
       *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * a4 + 4 * hl) = __builtin_convertvector(w, bf16x4);
     }
   if (p.lse && hl == 0)
-    p.lse[(int64_t)hq * p.total_q + si.cu_q + tq] = (mrun + log2f(lt)) * 0.69314718055994531f;
+    p.lse[(int64_t)hq * p.total_q + ic.cu_q + tq] = (mrun + log2f(lt)) * 0.69314718055994531f;
 }
 
 // ------------------------------------------------------------------------------------------------

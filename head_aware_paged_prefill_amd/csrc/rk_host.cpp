@@ -156,6 +156,7 @@ struct rk_tables {
     const int32_t *page_ids;
     const uint8_t *head_class;
     const rk::Item *items;
+    const rk::ItemCtx *ictx;
     const int32_t *app;
     const rk::MassUnit *mass_units;
     const rk::DecItem *dec_items;
@@ -183,7 +184,7 @@ namespace {
 // Device workspace layout of one build.  Offsets are relative to the workspace base.
 struct WsLayout {
   size_t seqs = 0;
-  std::vector<size_t> page_base, page_ids, head_class, items, app, mass, dec_items, dec_comb;
+  std::vector<size_t> page_base, page_ids, head_class, items, ictx, app, mass, dec_items, dec_comb;
   size_t part_o = 0, part_lse = 0;  // decode-shaped calls only
   size_t pack_ids = 0;              // the held pages in hand-off order
   size_t total = 0;
@@ -277,6 +278,8 @@ WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, CallSched *sched)
     w.items.push_back(off);
     // the XCD-interleaved schedule pads short bins: at most kXcd slots per real item
     off = align_up(off + sizeof(rk::Item) * std::max<int64_t>(1, n_items * pd.num_kv_heads * kXcd));
+    w.ictx.push_back(off);
+    off = align_up(off + sizeof(rk::ItemCtx) * std::max<int64_t>(1, n_items * pd.num_kv_heads * kXcd));
     w.app.push_back(off);
     off = align_up(off + 2 * sizeof(int32_t) * std::max<int64_t>(1, n_app));
     rk::SchedInput si{bd->num_seqs, pd.num_kv_heads, T, pd.head_dim, pd.dtype == RK_F32 ? 4 : 2, bd->sink, bd->window,
@@ -503,6 +506,23 @@ hipError_t fill_and_upload(rk_tables *t, const WsLayout &ws, void *d_ws, void *s
       }
     std::memcpy(h + ws.head_class[li], &t->head_class[(size_t)l * t->Hkv], t->Hkv);
     std::memcpy(h + ws.items[li], t->items[li].data(), sizeof(rk::Item) * t->items[li].size());
+    {
+      rk::ItemCtx *ctx = reinterpret_cast<rk::ItemCtx *>(h + ws.ictx[li]);
+      const uint8_t *cls = &t->head_class[(size_t)l * t->Hkv];
+      const int32_t lg = log2i(t->P);
+      for (size_t i = 0; i < t->items[li].size(); ++i) {
+        const rk::Item &it = t->items[li][i];
+        if (it.seq < 0) {
+          ctx[i] = {-1, 0, 0, 0, 0, 0, 0, 0};
+          continue;
+        }
+        const int32_t b = it.seq, g = it.kv_head;
+        const int32_t qb = t->q_begin[b], L = t->kv_len[b], nq = L - qb;
+        const int32_t i_max = qb + std::min(it.tok0 + t->T, nq) - 1;
+        const int32_t po = pbase[g * t->num_seqs + b];
+        ctx[i] = {g | ((int32_t)cls[g] << 16), it.tok0, t->cu_q[b], qb, nq, L, po, pids[po + (i_max >> lg)]};
+      }
+    }
     std::memcpy(h + ws.app[li], t->app_items[li].data(), sizeof(int32_t) * t->app_items[li].size());
     std::memcpy(h + ws.mass[li], t->mass_units[li].data(), sizeof(rk::MassUnit) * t->mass_units[li].size());
     const rk::DecItem *dec_items = nullptr;
@@ -517,6 +537,7 @@ hipError_t fill_and_upload(rk_tables *t, const WsLayout &ws, void *d_ws, void *s
                   reinterpret_cast<const int32_t *>(dbase + ws.page_ids[li]),
                   reinterpret_cast<const uint8_t *>(dbase + ws.head_class[li]),
                   reinterpret_cast<const rk::Item *>(dbase + ws.items[li]),
+                  reinterpret_cast<const rk::ItemCtx *>(dbase + ws.ictx[li]),
                   reinterpret_cast<const int32_t *>(dbase + ws.app[li]),
                   reinterpret_cast<const rk::MassUnit *>(dbase + ws.mass[li]),
                   dec_items,
@@ -1088,6 +1109,7 @@ rk_status rk_seg_attn_prefill(rk_pool *pool, const rk_tables *t, int32_t layer, 
   p.page_ids = d.page_ids;
   p.seqs = t->d_seqs;
   p.items = d.items;
+  p.ictx = d.ictx;
   p.head_class = d.head_class;
   p.n_items = (int32_t)t->items[li].size();
   p.num_seqs = t->num_seqs;

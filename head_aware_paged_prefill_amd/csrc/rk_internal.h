@@ -36,6 +36,20 @@ struct Item {
   int32_t tiles;  // key tiles the item visits (its cost)
 };
 
+// Everything the attention kernel needs to start one item, in one 32-byte record the host fills
+// in launch order: reading it is the only memory round trip before the item's page ids and queries
+// (the item record, its sequence, its page-table base and its fallback page were four).
+struct ItemCtx {
+  int32_t kvh_cls;   // KV head | class << 16; -1 for schedule padding
+  int32_t tok0;      // first query index within the sequence's packed rows
+  int32_t cu_q;      // first packed row of the sequence
+  int32_t q_start;   // position of the sequence's first packed row
+  int32_t n_q;       // packed rows of the sequence
+  int32_t kv_len;
+  int32_t page_off;  // offset of the (KV head, seq) logical page table in page_ids
+  int32_t fallback;  // physical page of the item's last query (held, fully written)
+};
+
 // Visible key tiles of one item: sink tiles [0, ns) then window tiles [wt0, wt1].  For GLOBAL
 // heads ns = 0, wt0 = 0.  The host scheduler and the kernel both use this one definition.
 struct TileRange {
@@ -71,6 +85,7 @@ struct AttnParams {
   const int32_t *page_ids;   // logical page -> physical page, -1 when not held
   const SeqInfo *seqs;
   const Item *items;
+  const ItemCtx *ictx;        // per launch slot (bf16 kernel)
   const uint8_t *head_class;  // [Hkv] of this layer
   int32_t n_items;
   int32_t num_seqs;
