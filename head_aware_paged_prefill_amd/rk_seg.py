@@ -439,5 +439,15 @@ def rk_seg_unpack_pages(tables: Tables, seq: int, src, stream=None) -> None:
     _check(load().rk_seg_unpack_pages(tables.pool.handle, tables.handle, seq, _ptr(src), _nbytes(src), _stream(stream)))
 
 
+def rk_status_string(status: int) -> str:
+    """The status code's name, as the library spells it."""
+    return _status_name(status)
+
+
+def rk_last_error() -> str:
+    """The calling thread's message for its last failed call (empty if none failed)."""
+    return load().rk_last_error().decode()
+
+
 def rk_seg_version() -> str:
     return load().rk_seg_version().decode()

@@ -26,6 +26,9 @@ def test_library_exports_every_declared_function():
     for name in declared:
         assert hasattr(lib, name), name
     assert rk_seg.rk_seg_version().startswith("rk_seg")
+    import head_aware_paged_prefill_amd as pkg
+    for name in declared:  # the package re-exports every entry point's binding
+        assert callable(getattr(pkg, name, None)), name
 
 
 def host_pool(num_pages, free_order=None, num_layers=1, Hkv=2, D=64, P=16, dtype=rk_seg.RK_BF16):

@@ -1,7 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle, on an MI355X.
 
 Bars: bf16 output max-abs <= 2e-2 and mean-abs <= 2e-3 over all compared elements, row LSE within
-1e-3 * max(1, |lse|); fp32 storage max-abs 1e-4, mean-abs 1e-5, LSE 1e-5 * max(1, |lse|).  Integer
+1e-3 * max(1, |lse|); fp32 storage max-abs 1e-4, mean-abs 1e-5, LSE 1e-5 * max(1, |lse|).  The LSE
+bar is a relative error where |lse| >= 1 and an absolute one (floor 1) below.  Integer
 work (page tables, visible-key counts) is compared bit-exactly.  Re-rotated keys: within one bf16 ulp
 of the oracle's exact value.
 """
@@ -66,7 +67,7 @@ def check(o, lse, o_ref, lse_ref, dtype, what=""):
     assert err.max() <= mx_tol, "%s: max-abs %.3g" % (what, err.max())
     assert err.mean() <= mean_tol, "%s: mean-abs %.3g" % (what, err.mean())
     lerr = np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))
-    assert lerr.max() <= lse_tol, "%s: lse rel %.3g" % (what, lerr.max())
+    assert lerr.max() <= lse_tol, "%s: lse err %.3g (relative, absolute where |lse| < 1)" % (what, lerr.max())
 
 
 def full_parity(wl, what):
