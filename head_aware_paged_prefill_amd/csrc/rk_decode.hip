@@ -18,9 +18,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "rk_device.h"
 #include "rk_ops.h"
 #include "rk_seg.h"
+
+// Split-KV partials of the decode variant that allocates nothing: one array per GPU, a device global
+// of the code object, shared by every such call on that GPU and holding the last call's contents.
+// Host code never passes its name to a kernel (there it is a host-side stand-in): it passes the
+// address that hipGetSymbolAddress returned for the device.
+static __device__ __align__(256) float scratch[rk::kDecodeScratchBytes / sizeof(float)];
 
 namespace rk {
 namespace {
@@ -305,6 +313,25 @@ __global__ void __launch_bounds__(256) decode_combine(DecodeParams p) {
 }
 
 }  // namespace
+
+hipError_t decode_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // once per device, with that device current
+    void *a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t stream) {
   if (p.n_items <= 0) return hipSuccess;

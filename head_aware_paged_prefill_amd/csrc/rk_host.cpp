@@ -728,6 +728,71 @@ rk_status append_impl(rk_pool *pool, const rk_tables *t, int32_t layer, const vo
   return RK_OK;
 }
 
+// Decode of one layer; static_partials: the split-KV partials go to the per-GPU static array instead
+// of the tables' workspace, and nothing is allocated.
+rk_status decode_impl(rk_pool *pool, const rk_tables *t, int32_t layer, const void *q, const void *k_new,
+                      const void *v_new, void *o, float *lse, float softmax_scale, void *stream,
+                      bool static_partials) {
+  rk_status st = check_device_tables(pool, t, layer);
+  if (st != RK_OK) return st;
+  if (pool->desc.dtype != RK_BF16) return fail(RK_ERR_UNSUPPORTED, "decode needs a bf16 pool");
+  if (t->G > 16) return fail(RK_ERR_UNSUPPORTED, "decode supports at most 16 q heads per KV head");
+  if (!t->decode_shaped)
+    return fail(RK_ERR_STATE, "decode needs tables whose sequences have at most one query row each");
+  const int64_t total_q = t->cu_q[t->num_seqs];
+  if (total_q == 0) return RK_OK;
+  if (!q || !o || !aligned16(q) || !aligned16(o)) return fail(RK_ERR_INVALID_ARG, "q / o null or not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(RK_ERR_INVALID_ARG, "lse not 4-byte aligned");
+  if (!(softmax_scale <= 0.0f) && !std::isfinite(softmax_scale)) return fail(RK_ERR_INVALID_ARG, "softmax_scale not finite");
+  const int32_t li = layer - t->layer_begin;
+  float *part_o = t->d_part_o, *part_lse = t->d_part_lse;
+  if (static_partials) {  // checked before anything runs: a rejected call leaves the pool as it was
+    const int64_t slots = (int64_t)t->dec_items[li].size() / rk::kDecodeWaves;
+    const size_t o_bytes = align_up(sizeof(float) * slots * t->G * pool->desc.head_dim);
+    const size_t need = o_bytes + sizeof(float) * slots * t->G;
+    if (need > rk::kDecodeScratchBytes)
+      return fail(RK_ERR_UNSUPPORTED, "decode partials need %zu bytes, the static scratch holds %zu", need,
+                  rk::kDecodeScratchBytes);
+    void *base = nullptr;
+    hipError_t e = rk::decode_scratch(&base);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    part_o = static_cast<float *>(base);
+    part_lse = reinterpret_cast<float *>(static_cast<char *>(base) + o_bytes);
+  }
+  // both NULL: the caller appended the tokens already (rk_seg_append_kv); one NULL is an error
+  if (k_new || v_new) {
+    st = append_impl(pool, t, layer, k_new, v_new, stream);
+    if (st != RK_OK) return st;
+  }
+  const rk_tables::LayerDev &d = t->dev[li];
+  rk::DecodeParams p{};
+  p.q = q;
+  p.o = o;
+  p.lse = lse;
+  p.k_pages = pool->desc.k_pages;
+  p.v_pages = pool->desc.v_pages;
+  p.page_base = d.page_base;
+  p.page_ids = d.page_ids;
+  p.seqs = t->d_seqs;
+  p.items = d.dec_items;
+  p.comb_off = d.dec_comb;
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.num_seqs = t->num_seqs;
+  p.H = t->H;
+  p.Hkv = t->Hkv;
+  p.G = t->G;
+  p.P = t->P;
+  p.log2P = log2i(t->P);
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)pool->desc.head_dim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.total_q = (int32_t)total_q;
+  p.n_items = (int32_t)t->dec_items[li].size();
+  hipError_t e = rk::launch_decode(p, pool->desc.head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  return RK_OK;
+}
+
 }  // namespace
 
 #define RK_GUARD_BEGIN try {
@@ -1256,50 +1321,15 @@ rk_status rk_seg_unpack_pages(rk_pool *pool, const rk_tables *t, int32_t seq, co
 rk_status rk_seg_attn_decode(rk_pool *pool, const rk_tables *t, int32_t layer, const void *q, const void *k_new,
                              const void *v_new, void *o, float *lse, float softmax_scale, void *stream) {
   RK_GUARD_BEGIN
-  rk_status st = check_device_tables(pool, t, layer);
-  if (st != RK_OK) return st;
-  if (pool->desc.dtype != RK_BF16) return fail(RK_ERR_UNSUPPORTED, "decode needs a bf16 pool");
-  if (t->G > 16) return fail(RK_ERR_UNSUPPORTED, "decode supports at most 16 q heads per KV head");
-  if (!t->decode_shaped)
-    return fail(RK_ERR_STATE, "decode needs tables whose sequences have at most one query row each");
-  const int64_t total_q = t->cu_q[t->num_seqs];
-  if (total_q == 0) return RK_OK;
-  if (!q || !o || !aligned16(q) || !aligned16(o)) return fail(RK_ERR_INVALID_ARG, "q / o null or not 16-byte aligned");
-  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(RK_ERR_INVALID_ARG, "lse not 4-byte aligned");
-  if (!(softmax_scale <= 0.0f) && !std::isfinite(softmax_scale)) return fail(RK_ERR_INVALID_ARG, "softmax_scale not finite");
-  // both NULL: the caller appended the tokens already (rk_seg_append_kv); one NULL is an error
-  if (k_new || v_new) {
-    st = append_impl(pool, t, layer, k_new, v_new, stream);
-    if (st != RK_OK) return st;
-  }
-  const int32_t li = layer - t->layer_begin;
-  const rk_tables::LayerDev &d = t->dev[li];
-  rk::DecodeParams p{};
-  p.q = q;
-  p.o = o;
-  p.lse = lse;
-  p.k_pages = pool->desc.k_pages;
-  p.v_pages = pool->desc.v_pages;
-  p.page_base = d.page_base;
-  p.page_ids = d.page_ids;
-  p.seqs = t->d_seqs;
-  p.items = d.dec_items;
-  p.comb_off = d.dec_comb;
-  p.part_o = t->d_part_o;
-  p.part_lse = t->d_part_lse;
-  p.num_seqs = t->num_seqs;
-  p.H = t->H;
-  p.Hkv = t->Hkv;
-  p.G = t->G;
-  p.P = t->P;
-  p.log2P = log2i(t->P);
-  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)pool->desc.head_dim);
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.total_q = (int32_t)total_q;
-  p.n_items = (int32_t)t->dec_items[li].size();
-  hipError_t e = rk::launch_decode(p, pool->desc.head_dim, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-  return RK_OK;
+  return decode_impl(pool, t, layer, q, k_new, v_new, o, lse, softmax_scale, stream, false);
+  RK_GUARD_END
+}
+
+rk_status rk_seg_attn_decode_noalloc(rk_pool *pool, const rk_tables *t, int32_t layer, const void *q,
+                                     const void *k_new, const void *v_new, void *o, float *lse, float softmax_scale,
+                                     void *stream) {
+  RK_GUARD_BEGIN
+  return decode_impl(pool, t, layer, q, k_new, v_new, o, lse, softmax_scale, stream, true);
   RK_GUARD_END
 }
 

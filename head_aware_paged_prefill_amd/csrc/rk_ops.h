@@ -4,6 +4,7 @@
 #pragma once
 
 #include "rk_internal.h"
+#include "rk_seg.h"
 
 namespace rk {
 
@@ -131,6 +132,10 @@ struct PageCopyParams {
 
 hipError_t launch_page_copy(const PageCopyParams &p, bool pack, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, int head_dim, hipStream_t stream);
+// Size of the per-GPU static partials array of the decode variant that allocates nothing, and its
+// device address on the current device (looked up on the first call per device, then cached).
+constexpr size_t kDecodeScratchBytes = RK_DECODE_SCRATCH_BYTES;
+hipError_t decode_scratch(void **ptr);
 hipError_t launch_key_mass(const MassParams &p, int head_dim, hipStream_t stream);
 hipError_t launch_append(const KvWriteParams &p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_import(const KvWriteParams &p, int n_pages, int dtype, int head_dim, hipStream_t stream);

@@ -35,7 +35,8 @@ EXPORTS = [
     "rk_seg_tables_workspace_bytes", "rk_seg_build_tables", "rk_seg_tables_export", "rk_seg_tables_schedule",
     "rk_seg_tables_mass_schedule", "rk_seg_tables_stats", "rk_seg_tables_trim", "rk_seg_tables_destroy", "rk_seg_reuse_rerotate",
     "rk_seg_append_kv", "rk_seg_attn_prefill", "rk_seg_key_mass", "rk_seg_tables_advance_workspace_bytes",
-    "rk_seg_tables_advance", "rk_seg_tables_decode_schedule", "rk_seg_attn_decode", "rk_seg_pack_ledger",
+    "rk_seg_tables_advance", "rk_seg_tables_decode_schedule", "rk_seg_attn_decode", "rk_seg_attn_decode_noalloc",
+    "rk_seg_pack_ledger",
     "rk_seg_pack_pages", "rk_seg_unpack_pages", "rk_status_string",
     "rk_last_error", "rk_seg_version",
 ]
@@ -106,6 +107,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rk_seg_tables_advance": [VP, VP, P(I32), VP, ctypes.c_size_t, VP],
         "rk_seg_tables_decode_schedule": [VP, I32, P(I32), I64, P(I64), P(I32), I64],
         "rk_seg_attn_decode": [VP, VP, I32, VP, VP, VP, VP, VP, ctypes.c_float, VP],
+        "rk_seg_attn_decode_noalloc": [VP, VP, I32, VP, VP, VP, VP, VP, ctypes.c_float, VP],
         "rk_seg_pack_ledger": [VP, I32, P(PackLedger)],
         "rk_seg_pack_pages": [VP, VP, I32, VP, ctypes.c_size_t, VP],
         "rk_seg_unpack_pages": [VP, VP, I32, VP, ctypes.c_size_t, VP],
@@ -415,6 +417,17 @@ def rk_seg_attn_decode(tables: Tables, layer: int, q, k_new, v_new, o, lse=None,
     [total_q][H][D] bf16 (one row per sequence with a query); lse: [H][total_q] fp32."""
     _check(load().rk_seg_attn_decode(tables.pool.handle, tables.handle, layer, _ptr(q), _ptr(k_new), _ptr(v_new),
                                      _ptr(o), _ptr(lse), float(softmax_scale), _stream(stream)))
+
+
+RK_DECODE_SCRATCH_BYTES = 32 << 20  # the static partials array of rk_seg_attn_decode_noalloc, per GPU
+
+
+def rk_seg_attn_decode_noalloc(tables: Tables, layer: int, q, k_new, v_new, o, lse=None, softmax_scale: float = 0.0,
+                               stream=None) -> None:
+    """rk_seg_attn_decode with its partials in the library's static per-GPU array: allocates nothing.
+    Calls on one GPU that overlap in time race on that array."""
+    _check(load().rk_seg_attn_decode_noalloc(tables.pool.handle, tables.handle, layer, _ptr(q), _ptr(k_new),
+                                             _ptr(v_new), _ptr(o), _ptr(lse), float(softmax_scale), _stream(stream)))
 
 
 def rk_seg_pack_ledger(tables: Tables, seq: int = -1) -> dict:

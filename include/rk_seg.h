@@ -344,6 +344,23 @@ rk_status rk_seg_attn_decode(rk_pool *pool, const rk_tables *tables, int32_t lay
                              const void *k_new, const void *v_new, void *o, float *lse,
                              float softmax_scale, void *stream);
 
+/* rk_seg_attn_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, kernels and result; the
+ * split-KV partials go to a static array of RK_DECODE_SCRATCH_BYTES per GPU (a device global of the
+ * library, held until the process ends) instead of the tables' workspace, and the call allocates
+ * nothing (device or host).  Its address is looked up once per device, on the first call with that
+ * device current.  Every call on one GPU shares that array and leaves its contents behind; each
+ * call writes every partial it reads, so nothing has to start at zero.  Calls that overlap in time
+ * on one GPU (other streams, other threads) race on the array: order them.
+ * The partials take align256(slots * G * head_dim * 4) + slots * G * 4 bytes, slots = the layer's
+ * decode items / 4 (rk_seg_tables_decode_schedule), G = num_q_heads / num_kv_heads.
+ * Errors: those of rk_seg_attn_decode; RK_ERR_UNSUPPORTED when the partials exceed
+ *   RK_DECODE_SCRATCH_BYTES (checked before anything runs). */
+#define RK_DECODE_SCRATCH_BYTES (32u << 20)
+rk_status rk_seg_attn_decode_noalloc(rk_pool *pool, const rk_tables *tables, int32_t layer, const void *q,
+                                     const void *k_new, const void *v_new, void *o, float *lse,
+                                     float softmax_scale, void *stream);
+
 /* -- page hand-off (page "小红书把 KV Cache 按「头」拆了…" (zhichai.net), section 事件内容, and page
  *    "RedKnot – 小红书研发并开源的长上下文大模型推理引擎" (shshi.cn), section RedKnot核心特点: the
  *    prefill/decode KV transfer shrinks because only the pages a head keeps are sent) ------------ */

@@ -31,6 +31,12 @@ def test_library_exports_every_declared_function():
         assert callable(getattr(pkg, name, None)), name
 
 
+def test_static_decode_scratch_size_matches_the_header():
+    header = open(os.path.join(ROOT, "include", "rk_seg.h")).read()
+    m = re.search(r"#define RK_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", header)
+    assert m and int(m.group(1)) << int(m.group(2)) == rk_seg.RK_DECODE_SCRATCH_BYTES
+
+
 def host_pool(num_pages, free_order=None, num_layers=1, Hkv=2, D=64, P=16, dtype=rk_seg.RK_BF16):
     return rk_seg.rk_seg_pool_create(num_layers, Hkv, D, P, num_pages, dtype, None, None, free_order)
 
