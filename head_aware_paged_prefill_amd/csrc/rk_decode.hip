@@ -14,6 +14,9 @@
 //    workgroup writes one normalised partial output and lse.
 //  * decode_combine<D>: merges the partials of each query row: lse = log sum_s e^{lse_s},
 //    o = sum_s e^{lse_s - lse} o_s (the split-KV combine), one workgroup per row.
+//  * The new token (position kv_len - 1) of each sequence: when the caller passes it, the one item of a
+//    (seq, kv head) whose range ends at kv_len writes it into its page, with the slot clearing of the
+//    append kernel, and computes with it from registers; no wave reads a slot this launch writes.
 // Decode reads every visible K/V byte once, so it is bound by HBM bandwidth, not by the MFMAs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,6 +37,7 @@ namespace rk {
 namespace {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(4))) const int32_t ConstI32;  // read-only for the kernel's lifetime
 
 // max / sum over the four 16-lane groups (lanes c16, c16 + 16, c16 + 32, c16 + 48), with lane swaps
 // (no LDS traffic)
@@ -57,13 +61,57 @@ struct DecTile {
   u32x2 vb[D / 16];     // the same, keys kt + 16 + 4 (lane / 16) .. + 3
 };
 
+// The append of one (seq, kv head)'s new token at position j into page pg, by one wave: K row j and V
+// column j, then the clearing the append kernel does, so that every slot attention may load is finite:
+// the slots past kv_len = j + 1, and on a LOCAL head the slots of the page below its window and above
+// the sink.  The V chunk (8 slots) holding j is read, merged and written back; it holds earlier tokens.
+template <int D>
+__device__ void write_new_token(const DecodeParams &p, int pg, int j, int g, const bf16_t *kr, const bf16_t *vr,
+                                int lane) {
+  const int P = p.P, lp = j >> p.log2P, s = j & (P - 1);
+  bf16_t *kp = static_cast<bf16_t *>(const_cast<void *>(p.k_pages)) + (int64_t)pg * P * D;
+  bf16_t *vp = static_cast<bf16_t *>(const_cast<void *>(p.v_pages)) + (int64_t)pg * D * P;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // K rows [s, P): row s from the source, the rest zero (16 bytes per lane and step)
+  for (int c = lane; c < (P - s) * (D / 8); c += 64) {
+    const int r = s + c / (D / 8), ch = c % (D / 8);
+    *reinterpret_cast<u32x4 *>(kp + (int64_t)r * D + 8 * ch) =
+        r == s ? *reinterpret_cast<const u32x4 *>(kr + 8 * ch) : zero;
+  }
+  // V channel rows, chunks of 8 slots from the one holding s: slot s from the source, later slots zero
+  const int cs = s >> 3, nch = P / 8 - cs;
+  for (int c = lane; c < D * nch; c += 64) {
+    const int d = c / nch, k = cs + c % nch;
+    bf16x8 *dst = reinterpret_cast<bf16x8 *>(vp + (int64_t)d * P + 8 * k);
+    bf16x8 w = {};
+    if (k == cs) {
+      const bf16x8 old = *dst;
+      const bf16_t v = vr[d];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = 8 * k + i < s ? old[i] : (8 * k + i == s ? v : bf16_t(0.f));
+    }
+    *dst = w;
+  }
+  // a LOCAL head: slots [max(page start, sink), kv_len - window) of the page
+  if (p.head_class[g] != RK_GLOBAL) {
+    const int z0 = max(lp * P, p.sink) - lp * P, z1 = min(j + 1 - p.window, j) - lp * P;
+    for (int c = lane; c < max(0, z1 - z0) * D; c += 64) {
+      const int r = z0 + c / D, d = c % D;
+      kp[(int64_t)r * D + d] = bf16_t(0.f);
+      vp[(int64_t)d * P + r] = bf16_t(0.f);
+    }
+  }
+}
+
 // SMALLP: 8-key pages, where a 16-key half of a tile spans two pages (each lane picks its page)
 template <int D, bool SMALLP>
-__global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p) {
+__global__ void __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2))) decode_bf16(DecodeParams p) {
   constexpr int KS = D / 32;  // 32-channel steps of QK
   constexpr int DT = D / 16;  // 16-channel tiles of PV
   constexpr int NW = kDecodeWaves;
-  __shared__ f32x4 sm_o[NW][16][D / 4];  // per wave: unnormalised O^T columns (query rows)
+  // per wave: unnormalised O^T columns (query rows); a row is padded by one 16-byte chunk so that the
+  // sixteen rows a store instruction writes (lanes c16) start in different banks
+  __shared__ f32x4 sm_o[NW][16][D / 4 + 1];
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, c16 = lane & 15, q4 = lane >> 4;
@@ -71,7 +119,10 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p)
   const int b = it.seq, g = it.kv_head, k0 = it.k0, k1 = it.k1;
   const SeqInfo si = p.seqs[b];
   const int L = si.kv_len, P = p.P, G = p.G;
-  const int32_t *pt = p.page_ids + p.page_base[g * p.num_seqs + b];
+  // the page table through the constant address space: the kernel never writes it, and so its
+  // uniform lookups compile to scalar loads (a vector load here would make the tile loop wait on
+  // vmcnt(0), i.e. on the next tile's prefetch, before every tile)
+  const ConstI32 *pt = (const ConstI32 *)(p.page_ids + p.page_base[g * p.num_seqs + b]);
   // a key past kv_len or on a page the head does not hold reads the page of k0 (held) and is masked
   const int pg0 = pt[k0 >> p.log2P];
   auto page_of = [&](int key) {  // uniform: a scalar load of the page table
@@ -98,6 +149,23 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p)
       bf16x8 z = {};
       qf[ks] = ok ? *reinterpret_cast<const bf16x8 *>(qrow + 32 * ks + 8 * q4) : z;
     }
+  }
+
+  // the call's new token, when this item owns it: kn (K channels 32 ks + 8 q4 .. + 7) and vn (V channel
+  // 16 dt + c16) patch its key in the last tile; the page gets the row and the append's clearing
+  const int jn = L - 1;
+  const bool own_new = p.k_src != nullptr && k1 == L && k1 > k0;  // uniform
+  bf16x8 kn[KS];
+  bf16_t vn[DT];
+  if (own_new) {
+    const int64_t row = ((int64_t)si.cu_q * p.Hkv + g) * D;
+    const bf16_t *kr = static_cast<const bf16_t *>(p.k_src) + row;
+    const bf16_t *vr = static_cast<const bf16_t *>(p.v_src) + row;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kn[ks] = *reinterpret_cast<const bf16x8 *>(kr + 32 * ks + 8 * q4);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vn[dt] = vr[16 * dt + c16];
+    write_new_token<D>(p, pt[jn >> p.log2P], jn, g, kr, vr, lane);
   }
 
   const char *kbytes = static_cast<const char *>(p.k_pages);
@@ -150,7 +218,33 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p)
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int kt, const DecTile<D> &T) {
+  // the owner's last tile: key jn from registers, keys past it zero in V (their slots may hold anything
+  // in this launch; a masked key weighs 0, and 0 times a non-finite value would not be 0)
+  auto patch = [&](int kt, DecTile<D> &T) {
+    const bool krow = c16 == (jn & 15);  // the lane holding K row jn (in half (jn - kt) / 16)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {  // static indices only: the tile stays in registers
+      const bool mine = krow && hh == ((jn - kt) >> 4);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) T.k[hh][ks] = mine ? kn[ks] : T.k[hh][ks];
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        bf16x4 r = __builtin_bit_cast(bf16x4, hh ? T.vb[dt] : T.va[dt]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kt + 16 * hh + 4 * q4 + i;
+          r[i] = key == jn ? vn[dt] : (key > jn ? bf16_t(0.f) : r[i]);
+        }
+        if (hh) T.vb[dt] = __builtin_bit_cast(u32x2, r);
+        else T.va[dt] = __builtin_bit_cast(u32x2, r);
+      }
+  };
+
+  auto compute = [&](int kt, DecTile<D> &T) {
+    if (own_new && kt == (jn & ~31)) patch(kt, T);
     f32x4 s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -192,25 +286,35 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p)
     }
   };
 
-  // tile t's loads are issued while tile t - 1 is computed; its page ids were looked up two tiles
-  // earlier (scalar loads stay in flight: no LDS instruction shares their wait counter)
+  // tile t + 1's loads are issued before tile t is computed; page ids are looked up two tiles before
+  // their loads.  The steady-state loop issues both of its loads on every pass (tiles t + 1 and
+  // t + 2 exist), so every path into a tile's first use has the same loads outstanding and the
+  // compiler's wait counts leave the next tile in flight; the last one or two tiles are peeled.
   const int t0 = k0 & ~31;
   const int ntiles = k1 > k0 ? ((k1 - 1 - t0) >> 5) + 1 : 0;  // a padding item has no keys
-  DecTile<D> buf[2];
-  Pages pn = pages_of(t0), pn2 = pages_of(t0 + 32);
-  if (ntiles > 0) load(t0, pn, buf[0]);
-  pn = pn2;
-  pn2 = pages_of(t0 + 64);
-  for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) load(t0 + 32 * (t + 1), pn, buf[1]);
+  if (ntiles > 0) {
+    DecTile<D> buf[2];
+    Pages pn = pages_of(t0), pn2 = pages_of(t0 + 32);
+    load(t0, pn, buf[0]);
     pn = pn2;
-    pn2 = pages_of(t0 + 32 * (t + 3));
-    compute(t0 + 32 * t, buf[0]);
-    if (t + 1 < ntiles) {
-      if (t + 2 < ntiles) load(t0 + 32 * (t + 2), pn, buf[0]);
+    pn2 = pages_of(t0 + 64);
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+      load(t0 + 32 * (t + 1), pn, buf[1]);
+      pn = pn2;
+      pn2 = pages_of(t0 + 32 * (t + 3));
+      compute(t0 + 32 * t, buf[0]);
+      load(t0 + 32 * (t + 2), pn, buf[0]);
       pn = pn2;
       pn2 = pages_of(t0 + 32 * (t + 4));
       compute(t0 + 32 * (t + 1), buf[1]);
+    }
+    if (t + 1 < ntiles) {
+      load(t0 + 32 * (t + 1), pn, buf[1]);
+      compute(t0 + 32 * t, buf[0]);
+      compute(t0 + 32 * (t + 1), buf[1]);
+    } else {
+      compute(t0 + 32 * t, buf[0]);
     }
   }
 
@@ -251,16 +355,17 @@ __global__ void __launch_bounds__(64 * kDecodeWaves) decode_bf16(DecodeParams p)
   }
 }
 
-// One workgroup per query row (seq, q head): lse = max + log sum_s e^{lse_s - max} and
-// o = sum_s e^{lse_s - lse} o_s over the row's partials s.  The partials are spread over NG groups
-// of D / 4 threads (each thread four channels), which are summed through LDS at the end; a thread
-// keeps U partial loads in flight (the combine of a long GLOBAL head is latency-bound otherwise).
+// One workgroup per query row (seq, q head): lse = log sum_s e^{lse_s} and o = sum_s e^{lse_s - lse} o_s
+// over the row's partials s, in one pass.  The partials are spread over NG groups of D / 4 threads
+// (each thread four channels); a group keeps a running (max m, weight sum w = sum e^{lse_s - m}, acc =
+// sum e^{lse_s - m} o_s), rescaled when m grows, with U partial loads in flight per thread (the combine
+// of a long GLOBAL head is latency-bound otherwise).  The groups are merged through LDS at the end.
 template <int D>
 __global__ void __launch_bounds__(256) decode_combine(DecodeParams p) {
   constexpr int TPG = D / 4;         // threads per group: one 16-byte chunk of a partial each
   constexpr int NG = 256 / TPG;      // groups
   constexpr int U = 8;               // partials in flight per thread
-  __shared__ float red[256];
+  __shared__ float sm_m[NG], sm_w[NG];
   __shared__ f32x4 part[NG][TPG];
   const int tid = threadIdx.x;
   const int G = p.G;
@@ -270,25 +375,8 @@ __global__ void __launch_bounds__(256) decode_combine(DecodeParams p) {
   const int s0 = p.comb_off[bg] / kDecodeWaves, s1 = p.comb_off[bg + 1] / kDecodeWaves;
   if (s0 == s1) return;  // the sequence has no query row
   const SeqInfo si = p.seqs[b];
-  auto block_reduce = [&](float v, bool is_max) {
-    red[tid] = v;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-      if (tid < w) red[tid] = is_max ? fmaxf(red[tid], red[tid + w]) : red[tid] + red[tid + w];
-      __syncthreads();
-    }
-    const float out = red[0];
-    __syncthreads();
-    return out;
-  };
-  float mx = -INFINITY;
-  for (int s = s0 + tid; s < s1; s += 256) mx = fmaxf(mx, p.part_lse[(int64_t)s * G + r]);
-  mx = block_reduce(mx, true);
-  float tot = 0.f;
-  for (int s = s0 + tid; s < s1; s += 256) tot += expf(p.part_lse[(int64_t)s * G + r] - mx);
-  tot = block_reduce(tot, false);
-  const float lse = mx + logf(tot);
   const int grp = tid / TPG, d4 = tid - grp * TPG;
+  float m = -INFINITY, w = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = s0 + grp; s < s1; s += NG * U) {
     f32x4 v[U];
@@ -297,18 +385,44 @@ __global__ void __launch_bounds__(256) decode_combine(DecodeParams p) {
     for (int u = 0; u < U; ++u) {
       const int su = min(s + NG * u, s1 - 1);  // past the row's last partial: reloaded, weight 0
       v[u] = *reinterpret_cast<const f32x4 *>(p.part_o + ((int64_t)su * G + r) * D + 4 * d4);
-      l[u] = p.part_lse[(int64_t)su * G + r];
+      l[u] = s + NG * u < s1 ? p.part_lse[(int64_t)su * G + r] : -INFINITY;
     }
+    float mu = m;
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc += (s + NG * u < s1 ? expf(l[u] - lse) : 0.f) * v[u];
+    for (int u = 0; u < U; ++u) mu = fmaxf(mu, l[u]);
+    const float sc = m == -INFINITY ? 0.f : expf(m - mu);  // mu is finite: the first pass has a partial
+    acc *= sc;
+    w *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float e = l[u] == -INFINITY ? 0.f : expf(l[u] - mu);
+      acc += e * v[u];
+      w += e;
+    }
+    m = mu;
+  }
+  if (d4 == 0) {
+    sm_m[grp] = m;
+    sm_w[grp] = w;
   }
   part[grp][d4] = acc;
   __syncthreads();
   if (grp == 0) {
-    for (int j = 1; j < NG; ++j) acc += part[j][d4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) mx = fmaxf(mx, sm_m[j]);
+    float tot = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const float e = sm_m[j] == -INFINITY ? 0.f : expf(sm_m[j] - mx);  // a group with no partial: 0
+      tot += e * sm_w[j];
+      o += e * part[j][d4];
+    }
+    o *= 1.0f / tot;
     const int64_t row = (int64_t)si.cu_q * p.H + g * G + r;
-    *reinterpret_cast<bf16x4 *>(static_cast<bf16_t *>(p.o) + row * D + 4 * d4) = __builtin_convertvector(acc, bf16x4);
-    if (d4 == 0 && p.lse) p.lse[(int64_t)(g * G + r) * p.total_q + si.cu_q] = lse;
+    *reinterpret_cast<bf16x4 *>(static_cast<bf16_t *>(p.o) + row * D + 4 * d4) = __builtin_convertvector(o, bf16x4);
+    if (d4 == 0 && p.lse) p.lse[(int64_t)(g * G + r) * p.total_q + si.cu_q] = mx + logf(tot);
   }
 }
 

@@ -759,10 +759,11 @@ rk_status decode_impl(rk_pool *pool, const rk_tables *t, int32_t layer, const vo
     part_o = static_cast<float *>(base);
     part_lse = reinterpret_cast<float *>(static_cast<char *>(base) + o_bytes);
   }
-  // both NULL: the caller appended the tokens already (rk_seg_append_kv); one NULL is an error
+  // both NULL: the caller appended the tokens already (rk_seg_append_kv); one NULL is an error.
+  // Otherwise the decode kernel appends them itself (the item that ends at kv_len writes its token).
   if (k_new || v_new) {
-    st = append_impl(pool, t, layer, k_new, v_new, stream);
-    if (st != RK_OK) return st;
+    if (!k_new || !v_new) return fail(RK_ERR_INVALID_ARG, "null k_new / v_new");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(RK_ERR_INVALID_ARG, "k_new / v_new not 16-byte aligned");
   }
   const rk_tables::LayerDev &d = t->dev[li];
   rk::DecodeParams p{};
@@ -778,6 +779,11 @@ rk_status decode_impl(rk_pool *pool, const rk_tables *t, int32_t layer, const vo
   p.comb_off = d.dec_comb;
   p.part_o = part_o;
   p.part_lse = part_lse;
+  p.k_src = k_new;
+  p.v_src = v_new;
+  p.head_class = d.head_class;
+  p.sink = t->sink;
+  p.window = t->window;
   p.num_seqs = t->num_seqs;
   p.H = t->H;
   p.Hkv = t->Hkv;

@@ -109,6 +109,13 @@ struct DecodeParams {
   const int32_t *comb_off;  // [num_seqs * Hkv + 1]: first item of (seq, kv head) = b * Hkv + g
   float *part_o;          // [n_items / kDecodeWaves][G][D] fp32, normalised partial outputs
   float *part_lse;        // [n_items / kDecodeWaves][G] fp32, natural log
+  // the new token of each sequence with a query row, [total_q][Hkv][D] bf16, or null when the caller
+  // appended it already: then the item that ends at kv_len writes it into its page
+  const void *k_src;
+  const void *v_src;
+  const uint8_t *head_class;  // [Hkv] classes of the layer
+  int32_t sink;
+  int32_t window;
   int32_t num_seqs;
   int32_t H;
   int32_t Hkv;

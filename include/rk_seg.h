@@ -330,10 +330,12 @@ rk_status rk_seg_key_mass(rk_pool *pool, const rk_tables *tables, int32_t layer,
 
 /* Decode for one layer of decode-shaped tables (every sequence has at most one query row, at
  * position kv_len - 1, e.g. after rk_seg_tables_advance with n_new = 1): append k_new / v_new
- * (as rk_seg_append_kv; skipped when both are NULL), then split-KV attention over the items of
- * rk_seg_tables_decode_schedule, each giving a partial (o_s, lse_s) over its key range, then the
- * combine o = sum_s e^{lse_s - lse} o_s, lse = log sum_s e^{lse_s} into o / lse.  The result is the
- * masked softmax attention of rk_seg_attn_prefill for those rows.
+ * (leaving the pages as rk_seg_append_kv would; skipped when both are NULL), split-KV attention over
+ * the items of rk_seg_tables_decode_schedule, each giving a partial (o_s, lse_s) over its key range,
+ * then the combine o = sum_s e^{lse_s - lse} o_s, lse = log sum_s e^{lse_s} into o / lse.  The result
+ * is the masked softmax attention of rk_seg_attn_prefill for those rows.  Two kernel launches: the
+ * append happens inside the attention kernel, by the item whose range ends at kv_len.
+ * k_new, v_new: device [total_q][num_kv_heads][head_dim] bf16, 16-byte aligned, both or neither.
  * q, o: device [total_q][num_q_heads][head_dim] bf16 (total_q = the sequences with a query row);
  * lse: device [num_q_heads][total_q] fp32 or NULL; softmax_scale <= 0 selects 1/sqrt(head_dim).
  * The partials live in the tables' workspace, so decode calls on one tables object are ordered on

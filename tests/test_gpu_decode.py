@@ -172,37 +172,53 @@ def test_decode_rejects_unsupported_and_prefill_shaped_tables():
         r.close()
 
 
-def test_decode_with_null_kv_after_explicit_append_is_bit_identical():
-    """rk_seg_attn_decode with k_new = v_new = NULL skips the append: after rk_seg_append_kv of the same
-    tokens it returns the bits of the call that appends them itself."""
-    wl = workloads.random_small(11, torch.bfloat16, allow_reuse=False)
-    say("decode NULL k/v: kv_lens=%s G=%d" % (wl.kv_lens, wl.group))
+@pytest.mark.parametrize("seed", [11, 23, 14])  # LOCAL W=16 < P=32; mixed, W=1, sink 4; mixed, P=64
+def test_decode_appending_itself_matches_explicit_append_bit_for_bit(seed):
+    """rk_seg_attn_decode given k_new / v_new appends the token inside the decode kernel; with k_new =
+    v_new = NULL it skips the append.  After rk_seg_append_kv of the same tokens the NULL call must
+    return the bits of the call that appends itself, step after step across page boundaries, and the
+    pool pages (with the append's clearing of slots past kv_len and, with a window shorter than a page,
+    below a LOCAL head's window) must end bit-identical too."""
+    wl = workloads.random_small(seed, torch.bfloat16, allow_reuse=False)
+    steps = 2 * wl.page_size + 3
+    say("decode self-append vs explicit: kv_lens=%s G=%d P=%d W=%d steps=%d" % (
+        wl.kv_lens, wl.group, wl.page_size, wl.window, steps))
     B = wl.num_seqs
-    inp = workloads.make_inputs(wl, num_pages=workloads.pool_pages_needed_hint(wl) + wl.pool_slack + 4 * B * wl.num_kv_heads)
+    inp = workloads.make_inputs(wl, num_pages=workloads.pool_pages_needed_hint(wl) + wl.pool_slack
+                                + 4 * B * wl.num_kv_heads * (steps // wl.page_size + 2))
     dinp = to_dev(inp)
     outs = []
     for explicit in (False, True):
         r = PrefillRunner(wl, free_order=inp.free_order, poison=True)
+        run = []
         try:
             r.build()
             r.attend(dinp.q, dinp.k_new, dinp.v_new)
             r.trim()
-            r.advance([1] * B)
-            q, k, v = workloads.decode_inputs(wl, 0, B)
-            q, k, v = q.cuda(), k.cuda(), v.cuda()
-            o = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=wl.dtype, device="cuda")
-            lse = torch.empty((wl.num_q_heads, B), dtype=torch.float32, device="cuda")
-            if explicit:
-                rk_seg.rk_seg_append_kv(r.tables, wl.layer, k, v)
-                rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, None, None, o, lse)
-            else:
-                rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, k, v, o, lse)
-            torch.cuda.synchronize()
-            outs.append((o.cpu(), lse.cpu()))
+            for st in range(steps):
+                r.advance([1] * B)
+                _poison_free_pages(r)
+                q, k, v = (t.cuda() for t in workloads.decode_inputs(wl, st, B))
+                o = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=wl.dtype, device="cuda")
+                lse = torch.empty((wl.num_q_heads, B), dtype=torch.float32, device="cuda")
+                if explicit:
+                    rk_seg.rk_seg_append_kv(r.tables, wl.layer, k, v)
+                    rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, None, None, o, lse)
+                else:
+                    rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, k, v, o, lse)
+                torch.cuda.synchronize()
+                assert torch.isfinite(o.float()).all(), "step %d" % st
+                run.append((o.cpu(), lse.cpu()))
             with pytest.raises(rk_seg.RkError) as ei:  # one of the two missing is an error
                 rk_seg.rk_seg_attn_decode(r.tables, wl.layer, q, k, None, o, lse)
             assert ei.value.status == rk_seg.RK_ERR_INVALID_ARG
+            held = torch.tensor(sorted(set(range(r.num_pages)) - set(rk_seg.rk_seg_pool_free_list(r.pool))),
+                                dtype=torch.long, device="cuda")
+            outs.append((run, r.k_pages.index_select(0, held).cpu(), r.v_pages.index_select(0, held).cpu()))
         finally:
             r.close()
-    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
-    assert torch.equal(outs[0][1], outs[1][1])
+    for st, ((o0, l0), (o1, l1)) in enumerate(zip(outs[0][0], outs[1][0])):
+        assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)), "o differs at step %d" % st
+        assert torch.equal(l0, l1), "lse differs at step %d" % st
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16)), "K pages differ"
+    assert torch.equal(outs[0][2].view(torch.int16), outs[1][2].view(torch.int16)), "V pages differ"
