@@ -145,6 +145,7 @@ struct rk_tables {
   std::vector<std::vector<rk::Item>> items;     // per layer of the call, in launch order
   std::vector<std::vector<int32_t>> app_items;  // per layer: (seq, logical page) pairs
   std::vector<std::vector<rk::MassUnit>> mass_units;  // per layer: per-key mass work units, launch order
+  std::vector<int32_t> mass_steps;                    // per layer: query steps per mass unit
   bool decode_shaped = false;                          // every sequence has at most one query row
   std::vector<std::vector<rk::DecItem>> dec_items;     // per layer: split-KV decode items, slot order
   std::vector<std::vector<int32_t>> dec_comb;          // per layer: first item of (seq, kv head)
@@ -193,6 +194,7 @@ struct WsLayout {
 // Host schedules computed while sizing the workspace.
 struct CallSched {
   std::vector<std::vector<rk::MassUnit>> mass;
+  std::vector<int32_t> mass_steps;
   bool decode = false;
   std::vector<std::vector<rk::DecItem>> dec;
   std::vector<std::vector<int32_t>> comb;
@@ -253,6 +255,7 @@ WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, CallSched *sched)
   decode = decode && G <= 16;
   if (sched) {
     sched->mass.assign(nl, {});
+    sched->mass_steps.assign(nl, rk::kMassChunkSteps);
     sched->decode = decode;
     sched->dec.assign(decode ? nl : 0, {});
     sched->comb.assign(decode ? nl : 0, {});
@@ -285,9 +288,13 @@ WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, CallSched *sched)
     rk::SchedInput si{bd->num_seqs, pd.num_kv_heads, T, pd.head_dim, pd.dtype == RK_F32 ? 4 : 2, bd->sink, bd->window,
                       &bd->head_class[(size_t)l * pd.num_kv_heads], bd->kv_len, bd->q_start, q_begin.data()};
     const int32_t mk = rk::mass_keys_per_unit(G), mt = rk::mass_tokens_per_step(G);
-    if (sched && G <= 16) rk::mass_schedule(si, mk, mt, sched->mass[l - bd->layer_begin]);
+    const int32_t ms = rk::mass_steps_per_chunk(si, mk, mt);
+    if (sched && G <= 16) {
+      rk::mass_schedule(si, mk, mt, ms, sched->mass[l - bd->layer_begin]);
+      sched->mass_steps[l - bd->layer_begin] = ms;
+    }
     w.mass.push_back(off);
-    off = align_up(off + sizeof(rk::MassUnit) * std::max<int64_t>(1, G <= 16 ? rk::mass_units_bound(si, mk, mt) : 0));
+    off = align_up(off + sizeof(rk::MassUnit) * std::max<int64_t>(1, G <= 16 ? rk::mass_units_bound(si, mk, mt, ms) : 0));
     if (decode) {
       if (sched) rk::decode_schedule(si, sched->dec[l - bd->layer_begin], sched->comb[l - bd->layer_begin]);
       dec_bound = rk::decode_items_bound(si);
@@ -368,6 +375,7 @@ rk_status prepare_tables(rk_pool *pool, const rk_batch_desc *bd, void *d_ws, siz
   std::unique_ptr<rk_tables> t(new rk_tables());
   t->pool = pool;
   t->mass_units = std::move(sched.mass);
+  t->mass_steps = std::move(sched.mass_steps);
   t->decode_shaped = sched.decode;
   t->dec_items = std::move(sched.dec);
   t->dec_comb = std::move(sched.comb);
@@ -986,7 +994,7 @@ rk_status rk_seg_tables_mass_schedule(const rk_tables *t, int32_t layer, int32_t
   const std::vector<rk::MassUnit> &v = t->mass_units[layer - t->layer_begin];
   if (n_units) *n_units = (int64_t)v.size();
   if (keys_per_unit) *keys_per_unit = rk::mass_keys_per_unit(t->G);
-  if (steps_per_chunk) *steps_per_chunk = rk::kMassChunkSteps;
+  if (steps_per_chunk) *steps_per_chunk = t->mass_steps[layer - t->layer_begin];
   if (tokens_per_step) *tokens_per_step = rk::mass_tokens_per_step(t->G);
   if (units)
     for (int64_t i = 0; i < std::min<int64_t>(cap, (int64_t)v.size()); ++i) {
@@ -1244,6 +1252,7 @@ rk_status rk_seg_key_mass(rk_pool *pool, const rk_tables *t, int32_t layer, cons
   if (units.size() > (size_t)INT32_MAX) return fail(RK_ERR_UNSUPPORTED, "per-key mass: too many work units");
   p.units = d.mass_units;
   p.n_units = (int32_t)units.size();
+  p.steps_per_chunk = t->mass_steps[layer - t->layer_begin];
   hipError_t e = rk::launch_key_mass(p, pool->desc.head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "key mass kernel launch");
   return RK_OK;

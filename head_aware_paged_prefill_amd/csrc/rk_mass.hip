@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(512, 1) key_mass_bf16(MassParams p) {
   int t_last = L - 1;
   if (!global && j0 >= SK) t_last = min(t_last, j0 + KEYS - 1 + W - 1);
   if (t_first > t_last) return;  // no query sees this block
-  constexpr int S = kMassChunkSteps;
+  const int S = p.steps_per_chunk;
   const int k_first = max((t_first - start) / T, u.qc * S), k_last = min((t_last - start) / T, u.qc * S + S - 1);
   if (k_first > k_last) return;
   const int nsteps = k_last - k_first + 1;

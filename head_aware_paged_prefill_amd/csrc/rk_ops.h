@@ -55,7 +55,7 @@ struct MassUnit {
   int32_t seq;  // < 0: padding
   int32_t kv_head;
   int32_t kblk;  // key block: keys kblk * mass_keys_per_unit(G) ..
-  int32_t qc;    // query chunk: steps qc * kMassChunkSteps .. of the head's token grid
+  int32_t qc;    // query chunk: steps qc * steps_per_chunk .. of the head's token grid
 };
 struct MassParams {
   const void *q;
@@ -80,9 +80,12 @@ struct MassParams {
   int32_t total_kv;
   const MassUnit *units;  // launch order
   int32_t n_units;
+  int32_t steps_per_chunk;  // query steps per unit (the layer's mass_steps_per_chunk)
 };
 constexpr int kMassRun = 16;         // units placed together on one XCD
-constexpr int kMassChunkSteps = 64;  // steps per query chunk
+constexpr int kMassChunkSteps = 64;      // steps per query chunk, at most
+constexpr int kMassMinChunkSteps = 4;    // ... and at least
+constexpr int kMassTargetUnits = 2048;   // units per layer below which the chunk is halved
 
 // Decode (one query row per sequence): split-KV work items, one wave each, over key ranges of the
 // query's visible set.  kDecodeWaves consecutive items belong to one (seq, kv head) (padding items

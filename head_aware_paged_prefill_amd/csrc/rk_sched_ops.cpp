@@ -7,7 +7,7 @@
 
 namespace rk {
 
-int64_t mass_units_bound(const SchedInput &t, int32_t keys, int32_t tokens) {
+int64_t mass_units_bound(const SchedInput &t, int32_t keys, int32_t tokens, int32_t S) {
   // any class: key blocks x query chunks from the earliest start (q_begin <= q_start), plus the
   // padding of the XCD bins (they differ by at most kMassRun units)
   int64_t n = 0;
@@ -15,14 +15,20 @@ int64_t mass_units_bound(const SchedInput &t, int32_t keys, int32_t tokens) {
     const int64_t L = t.kv_len[b], q = L - t.q_begin[b];
     if (q <= 0) continue;
     const int64_t steps = (q + tokens - 1) / tokens;
-    n += (int64_t)t.Hkv * ((L + keys - 1) / keys) * ((steps + kMassChunkSteps - 1) / kMassChunkSteps);
+    n += (int64_t)t.Hkv * ((L + keys - 1) / keys) * ((steps + S - 1) / S);
   }
   return n + (int64_t)kXcd * kMassRun;
 }
 
-void mass_schedule(const SchedInput &t, int32_t keys, int32_t tokens, std::vector<MassUnit> &units) {
+int32_t mass_steps_per_chunk(const SchedInput &t, int32_t keys, int32_t tokens) {
+  int32_t S = kMassChunkSteps;
+  while (S > kMassMinChunkSteps && mass_units_bound(t, keys, tokens, S) < kMassTargetUnits) S /= 2;
+  return S;
+}
+
+void mass_schedule(const SchedInput &t, int32_t keys, int32_t tokens, int32_t steps, std::vector<MassUnit> &units) {
   units.clear();
-  const int64_t S = kMassChunkSteps;
+  const int64_t S = steps;
   // runs of key blocks sharing (seq, kv head, query chunk), at most kMassRun long
   std::vector<std::vector<MassUnit>> runs;
   std::vector<std::vector<int32_t>> by_chunk;  // query chunk -> key blocks that need it

@@ -11,15 +11,21 @@
 
 namespace rk {
 
+// Query steps per work unit of the per-key mass pass for one layer: kMassChunkSteps, halved (down to
+// kMassMinChunkSteps) while the class-independent unit bound stays below kMassTargetUnits, so that a
+// small call still spreads over the chip instead of running a few long units.  A function of the
+// shape only, so the workspace bound and the schedule agree.
+int32_t mass_steps_per_chunk(const SchedInput &in, int32_t keys, int32_t tokens);
+
 // Work units of the per-key mass pass: key block kblk (`keys` keys) of (seq, kv head) over query
-// chunk qc (kMassChunkSteps steps of `tokens` tokens on the token grid from the head's class start).
+// chunk qc (`steps` steps of `tokens` tokens on the token grid from the head's class start).
 // Only units with a visible pair are listed.  Runs of at most kMassRun units with the same (seq, kv
 // head, qc) -- key blocks reading the same query rows -- are placed on one XCD, each run on the XCD
 // with the fewest units so far: launch position i runs on XCD i % kXcd; padding has seq = -1.
-void mass_schedule(const SchedInput &in, int32_t keys, int32_t tokens, std::vector<MassUnit> &units);
+void mass_schedule(const SchedInput &in, int32_t keys, int32_t tokens, int32_t steps, std::vector<MassUnit> &units);
 
 // An upper bound of mass_schedule's list length that holds for any head classes (head_class unused).
-int64_t mass_units_bound(const SchedInput &in, int32_t keys, int32_t tokens);
+int64_t mass_units_bound(const SchedInput &in, int32_t keys, int32_t tokens, int32_t steps);
 
 // Decode-shaped calls (every sequence has at most one query row, at position kv_len - 1): split-KV
 // items over the query's visible key ranges (GLOBAL: [0, L); LOCAL: [0, min(S, L)) and
