@@ -142,14 +142,14 @@ def test_decode_items_cover_the_visible_keys_once(seed):
             assert (cover == vis.astype(np.int64)).all(), "items must cover each visible key exactly once"
             ks = real[:, 2:].tolist()
             assert ks == sorted(ks)
-    # one key chunk, aiming the layer at 8192 items: a multiple of 32, at least 128; no item crosses
+    # one key chunk, aiming the layer at 8192 items: a multiple of 32, at least 192; no item crosses
     # a multiple of it
     keys = sum(int(attention.visibility_mask(int(c["hc"][0, g]), np.array([L - 1]), L, c["S"], c["W"]).sum())
                for b, L in enumerate(c["kv"]) if n_new[b] for g in range(Hkv))
     ranges = sum(len(_ranges(int(c["hc"][0, g]), L, c["S"], c["W"])) for b, L in enumerate(c["kv"]) if n_new[b]
                  for g in range(Hkv))
     room = max(8192 // 4, 8192 - 2 * ranges)
-    chunk = max(128, -(-(-(-keys // room)) // 32) * 32)
+    chunk = max(192, -(-(-(-keys // room)) // 32) * 32)
     real = items[items[:, 3] > items[:, 2]]
     assert len(real) <= 8192 or room == 8192 // 4
     for _, _, k0, k1 in real.tolist():
