@@ -287,8 +287,9 @@ WsLayout plan_ws(const rk_pool *pool, const rk_batch_desc *bd, CallSched *sched)
     off = align_up(off + 2 * sizeof(int32_t) * std::max<int64_t>(1, n_app));
     rk::SchedInput si{bd->num_seqs, pd.num_kv_heads, T, pd.head_dim, pd.dtype == RK_F32 ? 4 : 2, bd->sink, bd->window,
                       &bd->head_class[(size_t)l * pd.num_kv_heads], bd->kv_len, bd->q_start, q_begin.data()};
+    // the mass pass supports G <= 16 (above, no rows of a step fit and it has no units)
     const int32_t mk = rk::mass_keys_per_unit(G), mt = rk::mass_tokens_per_step(G);
-    const int32_t ms = rk::mass_steps_per_chunk(si, mk, mt);
+    const int32_t ms = G <= 16 ? rk::mass_steps_per_chunk(si, mk, mt) : rk::kMassChunkSteps;
     if (sched && G <= 16) {
       rk::mass_schedule(si, mk, mt, ms, sched->mass[l - bd->layer_begin]);
       sched->mass_steps[l - bd->layer_begin] = ms;
@@ -484,10 +485,18 @@ rk_status acquire_staging(rk_pool *pool, rk_tables *t, const WsLayout &ws) {
 }
 
 // Writes t's device view (pages assigned) into its staging and uploads it into d_ws on the stream.
+// Only the bytes written here travel: the regions are sized by bounds (the item lists for the
+// XCD-padded schedule, the mass units for any head classes), and every byte a kernel reads lies in a
+// written span.  Spans closer than kUploadGap are sent as one copy.
 hipError_t fill_and_upload(rk_tables *t, const WsLayout &ws, void *d_ws, void *stream) {
+  constexpr size_t kUploadGap = 256 << 10;
   char *h = static_cast<char *>(t->staging.ptr);
-  std::memset(h, 0, ws.total);
+  std::vector<std::pair<size_t, size_t>> spans;  // (offset, bytes) written
+  auto wrote = [&](size_t off, size_t bytes) {
+    if (bytes) spans.emplace_back(off, bytes);
+  };
   rk::SeqInfo *seqs = reinterpret_cast<rk::SeqInfo *>(h + ws.seqs);
+  wrote(ws.seqs, sizeof(rk::SeqInfo) * t->num_seqs);
   int64_t kv_off = 0;  // per-key outputs need it below 2^31 (checked where they are computed)
   for (int32_t b = 0; b < t->num_seqs; ++b) {
     seqs[b] = {t->q_begin[b], t->kv_len[b], t->cu_q[b], t->kv_len[b] - t->q_begin[b], t->q_start[b],
@@ -512,8 +521,13 @@ hipError_t fill_and_upload(rk_tables *t, const WsLayout &ws, void *d_ws, void *s
         for (int64_t i = t->held_off[k]; i < t->held_off[k + 1]; ++i) pids[off + t->held_logical[i]] = t->held_phys[i];
         off += nlog;
       }
+    wrote(ws.page_base[li], sizeof(int32_t) * t->Hkv * t->num_seqs);
+    wrote(ws.page_ids[li], sizeof(int32_t) * off);
     std::memcpy(h + ws.head_class[li], &t->head_class[(size_t)l * t->Hkv], t->Hkv);
+    wrote(ws.head_class[li], t->Hkv);
     std::memcpy(h + ws.items[li], t->items[li].data(), sizeof(rk::Item) * t->items[li].size());
+    wrote(ws.items[li], sizeof(rk::Item) * t->items[li].size());
+    wrote(ws.ictx[li], sizeof(rk::ItemCtx) * t->items[li].size());
     {
       rk::ItemCtx *ctx = reinterpret_cast<rk::ItemCtx *>(h + ws.ictx[li]);
       const uint8_t *cls = &t->head_class[(size_t)l * t->Hkv];
@@ -532,12 +546,16 @@ hipError_t fill_and_upload(rk_tables *t, const WsLayout &ws, void *d_ws, void *s
       }
     }
     std::memcpy(h + ws.app[li], t->app_items[li].data(), sizeof(int32_t) * t->app_items[li].size());
+    wrote(ws.app[li], sizeof(int32_t) * t->app_items[li].size());
     std::memcpy(h + ws.mass[li], t->mass_units[li].data(), sizeof(rk::MassUnit) * t->mass_units[li].size());
+    wrote(ws.mass[li], sizeof(rk::MassUnit) * t->mass_units[li].size());
     const rk::DecItem *dec_items = nullptr;
     const int32_t *dec_comb = nullptr;
     if (t->decode_shaped) {
       std::memcpy(h + ws.dec_items[li], t->dec_items[li].data(), sizeof(rk::DecItem) * t->dec_items[li].size());
       std::memcpy(h + ws.dec_comb[li], t->dec_comb[li].data(), sizeof(int32_t) * t->dec_comb[li].size());
+      wrote(ws.dec_items[li], sizeof(rk::DecItem) * t->dec_items[li].size());
+      wrote(ws.dec_comb[li], sizeof(int32_t) * t->dec_comb[li].size());
       dec_items = reinterpret_cast<const rk::DecItem *>(dbase + ws.dec_items[li]);
       dec_comb = reinterpret_cast<const int32_t *>(dbase + ws.dec_comb[li]);
     }
@@ -565,11 +583,19 @@ hipError_t fill_and_upload(rk_tables *t, const WsLayout &ws, void *d_ws, void *s
     }
     t->pack_off[t->num_seqs] = n;
     t->d_pack_ids = reinterpret_cast<const int32_t *>(dbase + ws.pack_ids);
+    wrote(ws.pack_ids, sizeof(int32_t) * n);
   }
   t->d_part_o = t->decode_shaped ? reinterpret_cast<float *>(dbase + ws.part_o) : nullptr;
   t->d_part_lse = t->decode_shaped ? reinterpret_cast<float *>(dbase + ws.part_lse) : nullptr;
   hipStream_t sm = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(d_ws, h, ws.total, hipMemcpyHostToDevice, sm);
+  std::sort(spans.begin(), spans.end());
+  hipError_t e = hipSuccess;
+  for (size_t i = 0; i < spans.size() && e == hipSuccess;) {
+    const size_t a = spans[i].first;
+    size_t z = a + spans[i].second;
+    for (++i; i < spans.size() && spans[i].first <= z + kUploadGap; ++i) z = std::max(z, spans[i].first + spans[i].second);
+    e = hipMemcpyAsync(dbase + a, h + a, z - a, hipMemcpyHostToDevice, sm);
+  }
   if (e == hipSuccess) e = hipEventRecord(t->ev, sm);
   if (e == hipSuccess) {
     t->d_ws = d_ws;

@@ -134,3 +134,18 @@ def test_workspace_size_does_not_depend_on_head_classes():
         assert len(sizes) == 1
     finally:
         rk_seg.rk_seg_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("G", [17, 32, 256])
+def test_groups_above_sixteen_have_no_mass_units(G):
+    # the mass pass supports at most 16 q heads per KV head: tables still build, with an empty unit list
+    pool = fake_pool(64, None, 1, 1, 64, 16)
+    ws = rk_seg.rk_seg_tables_workspace_bytes(pool, 0, 1, G, [0], [100], [[1]], 4, 16)
+    assert ws > 0
+    t = rk_seg.rk_seg_build_tables(pool, 0, 1, G, [0], [100], [[1]], 4, 16, device=False)
+    try:
+        units, K, T, S = rk_seg.rk_seg_tables_mass_schedule(t, 0)
+        assert len(units) == 0
+    finally:
+        rk_seg.rk_seg_tables_destroy(t)
+        rk_seg.rk_seg_pool_destroy(pool)
