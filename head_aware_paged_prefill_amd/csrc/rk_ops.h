@@ -93,7 +93,9 @@ constexpr int kMassTargetUnits = 2048;   // units per layer below which the chun
 // item / kDecodeWaves; the combine kernel merges the slots of each (seq, kv head).
 constexpr int kDecodeWaves = 4;           // items (waves) per workgroup
 constexpr int kDecodeTargetItems = 8192;  // items per layer the key chunk aims at (eight waves per SIMD)
-constexpr int kDecodeMinChunk = 192;      // keys
+constexpr int kDecodeMinChunk = 128;      // keys
+constexpr int kDecodeMinChunkLarge = 192;  // keys, for layers with at least kDecodeLargeKeys visible keys
+constexpr int64_t kDecodeLargeKeys = 65536;
 struct DecItem {
   int32_t seq;
   int32_t kv_head;

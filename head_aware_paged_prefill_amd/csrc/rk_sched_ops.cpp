@@ -118,7 +118,10 @@ void decode_schedule(const SchedInput &t, std::vector<DecItem> &items, std::vect
   // round of resident waves where they can
   const int64_t room = std::max<int64_t>(kDecodeTargetItems / 4, kDecodeTargetItems - 2 * ranges);
   int64_t chunk = (keys + room - 1) / room;
-  chunk = std::max<int64_t>(kDecodeMinChunk, (chunk + 31) / 32 * 32);
+  // a small layer is latency-bound and gains from more, shorter items; a large one needs longer key
+  // runs per wave to keep its loads in flight
+  const int64_t min_chunk = keys >= kDecodeLargeKeys ? kDecodeMinChunkLarge : kDecodeMinChunk;
+  chunk = std::max<int64_t>(min_chunk, (chunk + 31) / 32 * 32);
   for (int32_t b = 0; b < t.num_seqs; ++b)
     for (int32_t g = 0; g < t.Hkv; ++g) {
       comb_off[(size_t)b * t.Hkv + g] = (int32_t)items.size();

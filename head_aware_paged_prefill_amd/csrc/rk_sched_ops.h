@@ -31,7 +31,8 @@ int64_t mass_units_bound(const SchedInput &in, int32_t keys, int32_t tokens, int
 // items over the query's visible key ranges (GLOBAL: [0, L); LOCAL: [0, min(S, L)) and
 // [max(0, L - W), L), merged when they touch).  A range is cut at multiples of the key chunk, which
 // keeps the layer within kDecodeTargetItems items, two per range reserved for the cuts that do not
-// fall on a range boundary (at least kDecodeMinChunk keys, a multiple of 32).
+// fall on a range boundary (a multiple of 32, at least kDecodeMinChunk keys, or kDecodeMinChunkLarge
+// keys in a layer with at least kDecodeLargeKeys visible keys).
 // Items come grouped by (seq, kv head) in ascending key order, each group padded with empty items
 // (k0 = k1 = 0) to a multiple of kDecodeWaves; comb_off[b * Hkv + g] is the first item of (b, g) and
 // comb_off[num_seqs * Hkv] the item count.

@@ -87,12 +87,13 @@ def test_advance_matches_integer_oracle_bit_exact(seed):
     rk_seg.rk_seg_pool_destroy(pool)
 
 
-def _decode_case(rng):
+def _decode_case(rng, long=False):
     Hkv = int(rng.integers(1, 4))
     G = int(rng.choice([1, 4, 8, 16]))
     P = int(rng.choice([16, 64]))
     B = int(rng.integers(1, 5))
-    kv = [int(x) for x in rng.integers(1, 5000, size=B)]
+    # long: the layer may reach 65536 visible keys, where the larger minimum chunk applies
+    kv = [int(x) for x in rng.integers(20000, 70000, size=B)] if long else [int(x) for x in rng.integers(1, 5000, size=B)]
     S, W = int(rng.choice([0, 4, 40])), int(rng.choice([1, 64, 700, 3000]))
     hc = rng.integers(0, 2, size=(1, Hkv)).astype(np.uint8)
     return dict(Hkv=Hkv, G=G, P=P, kv=kv, S=S, W=W, hc=hc)
@@ -105,10 +106,10 @@ def _ranges(cls, L, S, W):
     return list(zip(edges[::2], edges[1::2]))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_decode_items_cover_the_visible_keys_once(seed):
     rng = np.random.Generator(np.random.PCG64(4400 + seed))
-    c = _decode_case(rng)
+    c = _decode_case(rng, long=seed >= 12)
     B, Hkv = len(c["kv"]), c["Hkv"]
     # one query row per sequence, except a sequence that does not advance (no row)
     n_new = [1 if rng.random() < 0.8 else 0 for _ in range(B)]
@@ -142,14 +143,15 @@ def test_decode_items_cover_the_visible_keys_once(seed):
             assert (cover == vis.astype(np.int64)).all(), "items must cover each visible key exactly once"
             ks = real[:, 2:].tolist()
             assert ks == sorted(ks)
-    # one key chunk, aiming the layer at 8192 items: a multiple of 32, at least 192; no item crosses
+    # one key chunk, aiming the layer at 8192 items: a multiple of 32, at least 128 (192 from 65536
+    # visible keys on); no item crosses
     # a multiple of it
     keys = sum(int(attention.visibility_mask(int(c["hc"][0, g]), np.array([L - 1]), L, c["S"], c["W"]).sum())
                for b, L in enumerate(c["kv"]) if n_new[b] for g in range(Hkv))
     ranges = sum(len(_ranges(int(c["hc"][0, g]), L, c["S"], c["W"])) for b, L in enumerate(c["kv"]) if n_new[b]
                  for g in range(Hkv))
     room = max(8192 // 4, 8192 - 2 * ranges)
-    chunk = max(192, -(-(-(-keys // room)) // 32) * 32)
+    chunk = max(192 if keys >= 65536 else 128, -(-(-(-keys // room)) // 32) * 32)
     real = items[items[:, 3] > items[:, 2]]
     assert len(real) <= 8192 or room == 8192 // 4
     for _, _, k0, k1 in real.tolist():
