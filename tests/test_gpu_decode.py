@@ -137,6 +137,16 @@ def test_decode_page_64():
     decode_parity(wl, 70, wl.name)
 
 
+def test_decode_single_long_sequence_takes_the_large_chunk():
+    # one 72K-token sequence: at least 65536 visible keys, so 192-key items; the GLOBAL heads' rows merge
+    # ~95 workgroup partials each in the combine, the LOCAL heads' window slides across page boundaries
+    wl = workloads.Workload(name="decode 1 x 72K 32q/4kv D=128", config_id=412, num_layers=1, layer=0,
+                            kv_lens=[72000], q_starts=[0], num_q_heads=32, num_kv_heads=4, head_dim=128,
+                            page_size=64, sink=4, window=3000, dtype=torch.bfloat16,
+                            head_class=np.array([[1, 0, 1, 0]], np.uint8), pool_slack=8)
+    decode_parity(wl, 3, wl.name, device_inputs=True)
+
+
 def test_llama70b_shape_decode_sampled():
     # the full 31 x 32K state; three sequences' rows checked against the oracle
     wl = workloads.llama70b()
