@@ -526,20 +526,42 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
     if (s + 1 < nsteps) step(s + 1, c1);
   }
 
-  // ---- epilogue: O^T accumulator (lane column = query, 16 channels per 32-channel block)
+  // ---- epilogue: O^T accumulator (lane column = query, 16 channels per 32-channel block).  The
+  // normalised rows go through LDS (the K image, free once every wave is past its last block), so
+  // each global store writes whole 16-byte chunks of D / 8 lanes per row: D / 8 rows per instruction
+  // instead of 32 rows with 8 bytes per lane.
   const float lt = halves_sum(lsum);
-  if (!valid) return;
   const float inv = 1.0f / lt;
-  bf16_t *orow = static_cast<bf16_t *>(p.o) + ((int64_t)(ic.cu_q + tq) * p.H + hq) * D;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;              // rows per store instruction
+  typedef __attribute__((address_space(3))) bf16x4 lds_b4;
+  typedef __attribute__((address_space(3))) int64_t lds_i64;
+  lds_u8 *const stage = lds_k + wave * 32 * D * 2;
+  lds_i64 *const rowoff = (lds_i64 *)&sm.ids[wave][0][0];
+  lds_barrier();
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       f32x4 w = {oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
                  oacc[db][4 * a4 + 3] * inv};
-      *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * a4 + 4 * hl) = __builtin_convertvector(w, bf16x4);
+      const int c = 4 * db + a4;
+      *(lds_b4 *)(stage + m * D * 2 + ((c ^ (m & (CPR - 1))) << 4) + 8 * hl) = __builtin_convertvector(w, bf16x4);
     }
-  if (p.lse && hl == 0)
+  if (hl == 0) rowoff[m] = valid ? ((int64_t)(ic.cu_q + tq) * p.H + hq) * D : (int64_t)-1;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  bf16_t *const obase = static_cast<bf16_t *>(p.o);
+  const int cl = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int rr = RPI * i + lane / CPR;
+    const bf16x8 v = *(lds_v8 *)(stage + rr * D * 2 + ((cl ^ (rr & (CPR - 1))) << 4));
+    const int64_t off = rowoff[rr];
+    if (off >= 0) *reinterpret_cast<bf16x8 *>(obase + off + 8 * cl) = v;
+  }
+  if (p.lse && valid && hl == 0)
     p.lse[(int64_t)hq * p.total_q + ic.cu_q + tq] = (mrun + log2f(lt)) * 0.69314718055994531f;
 }
 
