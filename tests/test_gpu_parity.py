@@ -105,6 +105,18 @@ def test_random_small_f32(seed):
     full_parity(workloads.random_small(seed, torch.float32), "random-small f32 %d" % seed)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_many_items_per_workgroup_bf16(seed):
+    """Hundreds of items: every persistent workgroup runs a chain of them (one-step items included),
+    so each item's first tiles come from the stream of the item before it."""
+    full_parity(workloads.random_many(seed, torch.bfloat16), "random-many bf16 %d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_random_many_items_per_workgroup_f32(seed):
+    full_parity(workloads.random_many(seed, torch.float32), "random-many f32 %d" % seed)
+
+
 def test_all_global_and_window_covering_local_equal_each_other():
     """The dense reference (every head GLOBAL) and LOCAL heads whose window covers the sequence agree."""
     wl = workloads.tiny(torch.bfloat16)

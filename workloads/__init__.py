@@ -216,6 +216,28 @@ def random_split(seed: int, dtype: torch.dtype = torch.bfloat16) -> Workload:
     return execute_split(wl, qg, name=wl.name)
 
 
+def random_many(seed: int, dtype: torch.dtype = torch.bfloat16) -> Workload:
+    """Seeded random batch of many short sequences: B in [48, 96], L in [1, 700] (a third of them up to
+    64 tokens, so one key tile), G in {4, 8}, Hkv in {2, 3}, D in {64, 128}, P in {8, 16, 64}, with
+    reuse and both head classes: several hundred work items, so every attention workgroup runs a chain
+    of items of every length, one-step items included."""
+    rng = np.random.Generator(np.random.PCG64(9000 + seed))
+    B = int(rng.integers(48, 97))
+    G = int(rng.choice([4, 8]))
+    Hkv = int(rng.integers(2, 4))
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([8, 16, 64]))
+    kv_lens = [int(rng.integers(1, 65)) if rng.random() < 1 / 3 else int(rng.integers(65, 701)) for _ in range(B)]
+    q_starts = [int(rng.integers(1, L)) if L > 1 and rng.random() < 0.3 else 0 for L in kv_lens]
+    S = int(rng.choice([0, 4, 17]))
+    W = int(rng.choice([16, 100, 257]))
+    hc = np.zeros((1, Hkv), np.uint8)
+    hc[0, int(rng.integers(0, Hkv))] = GLOBAL
+    return Workload(name="random-many seed %d" % seed, config_id=600 + seed, num_layers=1, layer=0,
+                    kv_lens=kv_lens, q_starts=q_starts, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                    page_size=P, sink=S, window=W, dtype=dtype, head_class=hc, pool_slack=7, doc_len=0)
+
+
 # ----------------------------------------------------------------------------------------------
 # random draws
 # ----------------------------------------------------------------------------------------------
