@@ -359,7 +359,7 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
       for (int c = 0; c < RING; ++c) kr[c] = read_k(bn, qn, c);
     }
     if constexpr (NEXT) sc[PR ^ 1] = f32x16{};
-    float sum, ev = 0.f;
+    float ev = 0.f, s2[4];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       if (i >= NC - RING) vr[i - (NC - RING)] = read_v(bc, qc, i - (NC - RING));
@@ -371,20 +371,23 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
       for (int u = 0; u < EPM; ++u) {
         const int k = i * EPM + u;
         const float w = weight(sc[PR][8 + k]);
-        sum = k == 0 ? w : sum + w;
-        if (k & 1) pk[PR][1][k >> 1] = pack(ev, w);
-        else ev = w;
+        if (k & 1) {
+          pk[PR][1][k >> 1] = pack(ev, w);
+          s2[k >> 1] = ev + w;
+        } else {
+          ev = w;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    return sum;
+    return (s2[0] + s2[1]) + (s2[2] + s2[3]);
   };
   // Phase B(j): O^T += V(j)^T P(j)^T beside the first-half weights of S(j+1); the last RING slices
   // read the first K operands of block j+2 (KPRE2) from buffer b2.
   auto phase_b = [&](auto nextc, auto kpre2c, auto par, auto bc, auto qc, auto b2, auto q2) {
     constexpr bool NEXT = decltype(nextc)::value, KPRE2 = decltype(kpre2c)::value;
     constexpr int PR = decltype(par)::value;
-    float sum = 0.f, ev = 0.f;
+    float ev = 0.f, s2[4];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       oacc[i % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % RING], __builtin_bit_cast(bf16x8, pk[PR][i / ND]),
@@ -398,14 +401,17 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
         for (int u = 0; u < EPM; ++u) {
           const int k = i * EPM + u;
           const float w = weight(sc[PR ^ 1][k]);
-          sum = k == 0 ? w : sum + w;
-          if (k & 1) pk[PR ^ 1][0][k >> 1] = pack(ev, w);
-          else ev = w;
+          if (k & 1) {
+            pk[PR ^ 1][0][k >> 1] = pack(ev, w);
+            s2[k >> 1] = ev + w;
+          } else {
+            ev = w;
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (NEXT) psum[PR ^ 1] = sum;
+    if constexpr (NEXT) psum[PR ^ 1] = (s2[0] + s2[1]) + (s2[2] + s2[3]);
   };
   // After phase A(j): accept block j's weights, or (rare) rescale to its true row max and redo them.
   auto settle = [&](auto par, float sum2) {
