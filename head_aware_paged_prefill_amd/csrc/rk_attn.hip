@@ -26,9 +26,11 @@
 //    block j's exponentials, and block j's PV product beside the first half of block j+1's.  Operand
 //    reads run four products ahead, across phases.
 //  * Online softmax in fp32 with exp2, without a per-block max: weights are taken against the running
-//    max, and only a block whose weight sum exceeds 2^8 (the one case where a weight can) rescales O
-//    and recomputes its weights against its true max.  Weights up to 2^8 are represented the same
-//    way in fp32 and bf16, so this is exact.
+//    max, and only a block whose weight sum exceeds 2^20 (the one case where a weight can) rescales O
+//    and recomputes its weights against its true max.  The reference point of the exponentials cancels
+//    in O / (row sum) and is added back in the lse, so any point at or below the true max gives the
+//    same result up to rounding (fp32 and bf16 keep their relative precision at any magnitude); the
+//    bound only keeps the row sum and O far inside the fp32 range.
 //  * Two 64-key tiles per LDS step, double-buffered, two barriers per step (K is consumed one block
 //    ahead of V).  Block classes come from indices: full (no per-element work) or edge (scores
 //    outside the row's visible set set to -inf in place); no mask tensor exists.
@@ -45,6 +47,7 @@ namespace {
 constexpr int BN = kKeyTile;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest un-normalised weight allowed (attn_f32)
+constexpr float kRescaleAt = 1048576.0f;  // 2^20: a lane's block weight sum that takes the rescale path
 
 // ------------------------------------------------------------------------------------------------
 // bf16 attention
@@ -81,9 +84,12 @@ __device__ __forceinline__ int vswz(int d, int Pt) {
 //   phase A(j): S(j+1) = K(j+1) Q^T (NC products)    beside the exponentials of the second half of S(j)
 //   phase B(j): O^T += V(j)^T P(j)^T (NC products)   beside the exponentials of the first half of S(j+1)
 // The running max is not taken per block: the exponentials use the current one, and a block whose
-// per-lane weight sum exceeds 2^8 (then, and only then, some weight may exceed 2^8) takes a rare
-// path that finds the block's true row max, rescales O and the row sum, and recomputes the block's
-// weights.  The first block of every row takes that path (the running max starts at -1e30).
+// per-lane weight sum exceeds kRescaleAt = 2^20 (then, and only then, some weight may exceed it)
+// takes a rare path that finds the block's true row max, rescales O and the row sum, and recomputes
+// the block's weights.  The first block of every row takes that path (the running max starts at
+// -1e30); later blocks only when their scores rise 20 (log2 units) above the running max.  With 2^8
+// a fifth of the blocks of rows whose keys carry 4x outliers took it.  Over at most 2^26 blocks of 16
+// keys per lane the row sum stays below 2^46, and O below 2^46 max|v|.
 // Operand reads run RING reads ahead of their products, across phases.  K is consumed one block
 // ahead of V, so a step has two barriers: X1 before the first product that reads the next buffer's
 // K (then the K tiles of the step after next are issued into this buffer), X2 before the first
@@ -417,14 +423,15 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
   auto settle = [&](auto par, float sum2) {
     constexpr int PR = decltype(par)::value;
     float tot = psum[PR] + sum2;
-    if (__any(tot > 256.0f)) {
+    if (__any(tot > kRescaleAt)) {
       float mt = sc[PR][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sc[PR][i]);
       const float mnew = fmaxf(mrun, halves_max(mt) * c2);
       const float alpha = fast_exp2(mrun - mnew);
+      mfma_result_wait();  // one wait for all tuples: the products that write them were issued before
 #pragma unroll
-      for (int db = 0; db < ND; ++db) in_place_scale(oacc[db], alpha);
+      for (int db = 0; db < ND; ++db) in_place_scale_ready(oacc[db], alpha);
       lsum *= alpha;
       mrun = mnew;
       tot = 0.f;

@@ -131,9 +131,9 @@ __device__ __forceinline__ void in_place_mask(f32x16 &s, uint32_t vis) {
   }
 }
 
-// v *= a for every element, in place
-__device__ __forceinline__ void in_place_scale(f32x16 &v, float a) {
-  mfma_result_wait();
+// v *= a for every element, in place, where the products writing v have already been waited for
+// (mfma_result_wait)
+__device__ __forceinline__ void in_place_scale_ready(f32x16 &v, float a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float x = v[i];
