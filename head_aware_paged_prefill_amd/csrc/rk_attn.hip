@@ -86,8 +86,10 @@ __device__ __forceinline__ int vswz(int d, int Pt) {
 // The running max is not taken per block: the exponentials use the current one, and a block whose
 // per-lane weight sum exceeds kRescaleAt = 2^20 (then, and only then, some weight may exceed it)
 // takes a rare path that finds the block's true row max, rescales O and the row sum, and recomputes
-// the block's weights.  The first block of every row takes that path (the running max starts at
-// -1e30); later blocks only when their scores rise 20 (log2 units) above the running max.  With 2^8
+// the block's weights.  A row's first visible block takes that path (the running max starts at
+// -1e30) when the row has no visible key in the item's first block; otherwise block 0 sets the
+// running max to its own row max.  Later blocks take it only when their scores rise 20 (log2 units)
+// above the running max.  With 2^8
 // a fifth of the blocks of rows whose keys carry 4x outliers took it.  Over at most 2^26 blocks of 16
 // keys per lane the row sum stays below 2^46, and O below 2^46 max|v|.
 // Operand reads run RING reads ahead of their products, across phases.  K is consumed one block
@@ -478,6 +480,12 @@ __global__ void __launch_bounds__(2 * kRowsPerItem, 1) attn_bf16(AttnParams p) {
     for (int c = 0; c < RING; ++c) kr[c] = read_k(IntC<0>{}, IntC<1>{}, c);
     const int jb0 = first_key(0, 0);
     if (!is_full(jb0)) mask_block(sc[0], jb0);
+    // the running max starts at this block's row max, so the block needs no rescale; a row with no
+    // visible key here keeps -1e30, and its first visible block takes the rescale path
+    float mt = sc[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sc[0][i]);
+    mrun = fmaxf(halves_max(mt) * c2, kNegBig);
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
