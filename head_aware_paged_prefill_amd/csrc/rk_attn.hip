@@ -34,6 +34,7 @@
 //  * Two 64-key tiles per LDS step, double-buffered, two barriers per step (K is consumed one block
 //    ahead of V).  Block classes come from indices: full (no per-element work) or edge (scores
 //    outside the row's visible set set to -inf in place); no mask tensor exists.
+//  * The normalised output rows go through LDS, so each store instruction writes whole rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
