@@ -117,6 +117,32 @@ def test_random_many_items_per_workgroup_f32(seed):
     full_parity(workloads.random_many(seed, torch.float32), "random-many f32 %d" % seed)
 
 
+@pytest.mark.parametrize("factor", [8.0, 24.0])
+def test_late_outlier_keys_take_the_rescale_path(factor):
+    """Key rows scaled up deep into a row lift its scores far above the running max taken so far
+    (8x: ~35, 24x: ~100 log2 units at the top, past the kernel's 2^20 rescale bound), so the rescale
+    path runs in the middle and at the end of rows of both head classes."""
+    wl = workloads.Workload(name="late outliers", config_id=950, num_layers=1, layer=0, kv_lens=[1500, 2100],
+                            q_starts=[0, 0], num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, sink=4,
+                            window=600, dtype=torch.bfloat16, head_class=np.array([[1, 0]], np.uint8), pool_slack=7)
+    inp = workloads.make_inputs(wl)
+    cu = wl.cu_q()
+    for b, L in enumerate(wl.kv_lens):
+        for pos in (700, 1400, L - 5):
+            inp.k_new[cu[b] + pos] = (inp.k_new[cu[b] + pos].float() * factor).to(wl.dtype)
+    full_parity_of(inp, "late outliers x%g" % factor)
+
+
+def full_parity_of(inp, what):
+    o_ref, lse_ref = reference.prefill(inp)
+    say(what)
+    r, o, lse = run_call(to_dev(inp))
+    try:
+        check(o, lse, o_ref, lse_ref, inp.wl.dtype, what)
+    finally:
+        r.close()
+
+
 def test_all_global_and_window_covering_local_equal_each_other():
     """The dense reference (every head GLOBAL) and LOCAL heads whose window covers the sequence agree."""
     wl = workloads.tiny(torch.bfloat16)
