@@ -250,7 +250,7 @@ def time_pack(b: "Bench", reps: int) -> dict:
 
 
 def run_workload(wl, steps: int, warmup: int, with_dense: bool, oracle_budget: float = 0.0, oracle_seed: int = 99,
-                 oracle_whole: bool = False):
+                 oracle_whole: bool = False, oracle_every_block: bool = False):
     log("workload: %s" % wl.name)
     # room for the decode step's new pages (one per (seq, kv head) at most)
     pages = workloads.pool_pages_needed_hint(wl) + wl.pool_slack + 2 * wl.num_seqs * wl.num_kv_heads
@@ -287,11 +287,12 @@ def run_workload(wl, steps: int, warmup: int, with_dense: bool, oracle_budget: f
                                                     co["parity"]["lse_err_max"]))
     elif oracle_budget > 0:
         torch.cuda.synchronize()
-        res["cpu_oracle"] = oracle_sample(wl, inp, b.o, b.lse, oracle_budget, oracle_seed)
+        res["cpu_oracle"] = oracle_sample(wl, inp, b.o, b.lse, oracle_budget, oracle_seed, full=oracle_every_block)
         co = res["cpu_oracle"]
-        log("  oracle on the host: %.4f TFLOP/s on %d threads over %d blocks; layer %.0f s extrapolated; "
+        log("  oracle on the host: %.4f TFLOP/s on %d threads over %d blocks; layer %.0f s %s; "
             "sampled-row parity max-abs %.3g mean-abs %.3g lse %.3g" % (
                 co["value"], co["cores"], co["blocks_sampled"], co["extrapolated_layer_s"],
+                "measured" if co["whole_layer"] else "extrapolated",
                 co["parity_on_sampled_rows"]["max_abs"], co["parity_on_sampled_rows"]["mean_abs"],
                 co["parity_on_sampled_rows"]["lse_err_max"]))
     log("  mixed: %.3f ms/step, attention %.3f ms, %.1f useful TFLOP/s (%.1f%% of bf16 peak)" % (
@@ -453,7 +454,7 @@ def blas_threads() -> int:
         return len(os.sched_getaffinity(0))
 
 
-def oracle_sample(wl, inp, o, lse, budget_s: float, seed: int) -> dict:
+def oracle_sample(wl, inp, o, lse, budget_s: float, seed: int, full: bool = False) -> dict:
     """The fp64 oracle (dense masked attention, oracle/) on a stratified sample of the call's 256-row
     blocks of (sequence, q head), on the call's own inputs, compared with the GPU's output on the same
     rows.  Strata: head class x position band (quarters of the sequence); every class contributes its
@@ -461,7 +462,10 @@ def oracle_sample(wl, inp, o, lse, budget_s: float, seed: int) -> dict:
     and its last block; then seeded random blocks until the time budget is spent.  The oracle computes
     each block densely over the whole sequence, so its time is proportional to rows x kv_len: the
     extrapolated layer time is that constant, fitted on the sample, times the layer's rows x kv_len,
-    plus building K/V once per (sequence, KV head)."""
+    plus building K/V once per (sequence, KV head).
+    full: every block instead, in (sequence, head) order so that each head's K/V is built once, with a
+    progress line every 30 s; the layer time is then measured (attention blocks + K/V builds), and the
+    parity covers every output of the call."""
     from oracle import attention as oatt
     from oracle import reference as oref
     D, G = wl.head_dim, wl.group
@@ -500,11 +504,14 @@ def oracle_sample(wl, inp, o, lse, budget_s: float, seed: int) -> dict:
                 must.append(pick)
     rng = np.random.Generator(np.random.PCG64(seed))
     rest = [blocks[i] for i in rng.permutation(len(blocks)) if blocks[i] not in must]  # without replacement
-    kv_cache, kv_build_s = {}, 0.0
+    kv_cache, kv_build_s, n_kv_built = {}, 0.0, 0
     t_att, work, pairs, n_blocks, per_stratum = 0.0, 0.0, 0.0, 0, {}
     err_max, err_sum, err_n, lse_rel = 0.0, 0.0, 0, 0.0
-    o_cpu = None
-    order = list(must)
+    if full:
+        order, rest = sorted(blocks, key=lambda x: (x[0], x[1], x[2])), []
+    else:
+        order = list(must)
+    t_start = t_last = time.perf_counter()
     while True:
         if order:
             blk = order.pop(0)
@@ -520,6 +527,10 @@ def oracle_sample(wl, inp, o, lse, budget_s: float, seed: int) -> dict:
             t0 = time.perf_counter()
             kv_cache[(b, g)] = oref.head_kv(inp, b, g)
             kv_build_s += time.perf_counter() - t0
+            n_kv_built += 1
+        if full and time.perf_counter() - t_last > 30.0:
+            t_last = time.perf_counter()
+            log("  oracle, every block: %d of %d done, %.0f s" % (n_blocks, len(blocks), t_last - t_start))
         k, v = kv_cache[(b, g)]
         rows = np.arange(r0, r1)
         q = oref.to64(inp.q[cu[b] + r0:cu[b] + r1, h])
@@ -541,13 +552,19 @@ def oracle_sample(wl, inp, o, lse, budget_s: float, seed: int) -> dict:
         lse_rel = max(lse_rel, float((np.abs(lg - lb) / np.maximum(1.0, np.abs(lb))).max()))  # relative; absolute below 1
     c = t_att / work
     n_kv = wl.num_seqs * wl.num_kv_heads
-    extrap = c * dense_work + (kv_build_s / max(1, len(kv_cache))) * n_kv if n_blocks else float("nan")
+    extrap = c * dense_work + (kv_build_s / max(1, n_kv_built)) * n_kv if n_blocks else float("nan")
+    if full:
+        extrap = t_att + kv_build_s  # measured, not extrapolated
+        what = ("every one of the %d 256-row blocks of (sequence, q head): the whole layer, %.1f s of fp64 NumPy "
+                "dense masked attention on the call's own inputs (+ %.1f s building K/V)" % (
+                    len(blocks), t_att, kv_build_s))
+    else:
+        what = ("%d of %d 256-row blocks of (sequence, q head), stratified by head class and position band, with "
+                "each class's first, S+W boundary and last blocks; %.1f s of fp64 NumPy dense masked attention "
+                "on the call's own inputs (+ %.1f s building K/V)" % (n_blocks, len(blocks), t_att, kv_build_s))
     return {"value": 4.0 * D * pairs / t_att / 1e12 if t_att > 0 else None,
             "unit": "TFLOP/s (useful: 4 D per visible pair)", "cores": blas_threads(), "kind": "oracle",
-            "sample": "%d of %d 256-row blocks of (sequence, q head), stratified by head class and position "
-                      "band, with each class's first, S+W boundary and last blocks; %.1f s of fp64 NumPy dense "
-                      "masked attention on the call's own inputs (+ %.1f s building K/V)" % (
-                          n_blocks, len(blocks), t_att, kv_build_s),
+            "sample": what, "whole_layer": bool(full),
             "blocks_sampled": n_blocks, "blocks_total": len(blocks), "strata_blocks": {
                 "%s/q%d" % ("global" if k[0] else "local", k[1]): v for k, v in sorted(strata.items())},
             "strata_sampled": per_stratum, "extrapolated_layer_s": extrap,
@@ -653,6 +670,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the dense reference, the other workloads and the reduced window sweep")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="run the oracle over every 256-row block of the workload's layer (minutes to hours of "
+                         "CPU time) instead of a sample, and check every output against it")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: the window x GLOBAL-head sweep at the 128K shape, "
                          "with a fit of layer time against visible pairs (one JSON line)")
@@ -679,7 +699,8 @@ def main():
         return
     wl = workloads.CONFIGS[a.workload]()
     cpu_s = 0.0 if a.no_cpu else a.cpu_seconds
-    main_res = run_workload(wl, a.steps, a.warmup, with_dense=not a.no_extra, oracle_budget=cpu_s)
+    main_res = run_workload(wl, a.steps, a.warmup, with_dense=not a.no_extra, oracle_budget=cpu_s,
+                            oracle_every_block=a.cpu_full)
     extra = {}
     short = max(2, a.steps // 2)
     if not a.no_extra:
