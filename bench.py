@@ -431,10 +431,13 @@ def sweep(steps: int, warmup: int, windows=(1024, 2048, 4096, 8192), globals_=(0
     torch.cuda.empty_cache()
     x = np.array([r["visible_pairs"] for r in rows], np.float64)
     y = np.array([r["ms_attention_median"] for r in rows], np.float64)
-    slope, icpt = np.polyfit(x, y, 1)
-    pred = icpt + slope * x
-    r2 = 1.0 - float(((y - pred) ** 2).sum()) / float(((y - y.mean()) ** 2).sum())
-    log("  fit: t = %.3f ms + %.4e ms/pair * pairs, R^2 = %.5f" % (icpt, slope, r2))
+    fit = None
+    if len(set(x.tolist())) >= 2:  # a fit needs two distinct pair counts (a one-row run is for profiling)
+        slope, icpt = np.polyfit(x, y, 1)
+        pred = icpt + slope * x
+        r2 = 1.0 - float(((y - pred) ** 2).sum()) / float(((y - y.mean()) ** 2).sum())
+        log("  fit: t = %.3f ms + %.4e ms/pair * pairs, R^2 = %.5f" % (icpt, slope, r2))
+        fit = {"intercept_ms": icpt, "ms_per_pair": slope, "r2": r2}
     per_class = {}
     for r in rows:
         if r["global_kv_heads"] in (0, 8):
@@ -443,7 +446,7 @@ def sweep(steps: int, warmup: int, windows=(1024, 2048, 4096, 8192), globals_=(0
                 "pct_hbm_peak_algorithmic": r["hbm"]["pct_hbm_peak_algorithmic"],
                 "pct_hbm_peak_tile": r["hbm"]["pct_hbm_peak_tile"]}
     return {"workload": base.name + " (window and GLOBAL-head sweep)", "steps": steps, "warmup": warmup,
-            "rows": rows, "fit": {"intercept_ms": icpt, "ms_per_pair": slope, "r2": r2}, "per_class": per_class}
+            "rows": rows, "fit": fit, "per_class": per_class}
 
 
 def blas_threads() -> int:
@@ -676,6 +679,10 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: the window x GLOBAL-head sweep at the 128K shape, "
                          "with a fit of layer time against visible pairs (one JSON line)")
+    ap.add_argument("--sweep-windows", default="1024,2048,4096,8192",
+                    help="windows of --sweep (comma-separated)")
+    ap.add_argument("--sweep-globals", default="0,1,2,4,8",
+                    help="GLOBAL KV-head counts of --sweep (comma-separated, 0..8)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size HBM reference for counters)")
     a = ap.parse_args()
@@ -695,7 +702,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if a.sweep:
-        print(json.dumps({"sweep": sweep(a.steps, a.warmup)}), flush=True)
+        windows = tuple(int(w) for w in a.sweep_windows.split(","))
+        globals_ = tuple(int(g) for g in a.sweep_globals.split(","))
+        if min(windows) < 1 or min(globals_) < 0 or max(globals_) > 8:
+            print("bench.py: windows must be >= 1 and GLOBAL KV-head counts in 0..8", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"sweep": sweep(a.steps, a.warmup, windows, globals_)}), flush=True)
         return
     wl = workloads.CONFIGS[a.workload]()
     cpu_s = 0.0 if a.no_cpu else a.cpu_seconds
